@@ -1,0 +1,201 @@
+"""CPU oracle for CSR sparse x dense products (fp64) and for the row plan.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package.  The HIP
+library and its Python binding never import it, and it imports nothing from
+them; the two share no code.
+
+Pages cited:
+  [IntelMax] "Performance Optimization of Deep Learning Sparse Matrix Kernels
+             on Intel Max Series GPU"
+  [Sgap]     "Sgap: Towards Efficient Sparse Tensor Algebra Compilation for GPU"
+
+Contents
+  spmm_ref   -- C = A*B and the bound S = |A|*|B| in fp64 ([IntelMax], SpMM
+                operation, Fig. 5 / Algorithm 2), computed by ``spmm_ref.c``.
+  plan_ref   -- the row-binning plan: which rows are short, medium or long, and
+                how long rows are cut into nnz chunks (see its docstring).
+  widen_bf16 -- exact bf16 -> float64 widening used by the oracle.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against values
+fixed by the mathematics (dense brute force, exact integer products, a
+hand-built worked example, invariants) rather than against itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "spmm_ref.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle_spmm.so")
+
+F32 = 0
+BF16 = 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``spmm_ref.c`` with gcc into ``liboracle_spmm.so``.
+
+    -ffp-contract=off keeps every a*b + acc a separate multiply and add, so
+    the fp64 results are reproducible.
+    """
+    if not force and os.path.exists(_LIB_PATH) and \
+            os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+           "-ffp-contract=off", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def load_library(path: str):
+    """Load an oracle shared library built from ``spmm_ref.c`` and declare
+    its functions."""
+    lib = ctypes.CDLL(path)
+    lib.oracle_spmm.restype = ctypes.c_int
+    lib.oracle_spmm.argtypes = [
+        ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_void_p,
+    ]
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        _lib = load_library(_LIB_PATH)
+    return _lib
+
+
+def num_threads() -> int:
+    """Threads the oracle's row loop uses (OpenMP)."""
+    return int(_load().oracle_num_threads())
+
+
+def _kind_of(arr: np.ndarray) -> int:
+    if arr.dtype == np.float32:
+        return F32
+    if arr.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"oracle takes float32 or bf16 bits (uint16), got {arr.dtype}")
+
+
+def spmm_ref(rowptr, colind, vals, B, N: int, rows=None, with_bound: bool = True,
+             library=None):
+    """fp64 oracle: rows of C = A*B and of the bound S = |A|*|B|.
+
+    [IntelMax], SpMM operation (Fig. 5, Algorithm 2): row C_i is the sum, over
+    the stored entries of row i in CSR order, of value * B[col, :].
+
+    rowptr, colind : int32 arrays (rowptr holds absolute offsets).
+    vals, B        : float32 arrays, or uint16 arrays holding bf16 bits.
+    B              : K x N, row-major (any shape whose flat layout is that).
+    rows           : None for every row, or an int array of row ids (a sample).
+    library        : a library from ``load_library`` (default: this oracle).
+    Returns (C, S) as float64 arrays of shape (len(rows) or M, N); S is None
+    when ``with_bound`` is False.
+    """
+    lib = _load() if library is None else library
+    rowptr = np.ascontiguousarray(rowptr, dtype=np.int32)
+    colind = np.ascontiguousarray(colind, dtype=np.int32)
+    vals = np.ascontiguousarray(vals)
+    B = np.ascontiguousarray(B)
+    M = rowptr.shape[0] - 1
+    if M < 0:
+        raise ValueError("rowptr must hold M+1 entries")
+    if rows is None:
+        rows_arr = None
+        count = M
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        count = rows_arr.shape[0]
+    C = np.empty((count, N), dtype=np.float64)
+    S = np.empty((count, N), dtype=np.float64) if with_bound else None
+    rc = lib.oracle_spmm(
+        M, N,
+        rowptr.ctypes.data, colind.ctypes.data,
+        _kind_of(vals), vals.ctypes.data,
+        _kind_of(B), B.ctypes.data,
+        None if rows_arr is None else rows_arr.ctypes.data, count,
+        C.ctypes.data, None if S is None else S.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_spmm rejected its arguments")
+    return C, S
+
+
+def widen_bf16(bits) -> np.ndarray:
+    """bf16 bit patterns -> float64, exactly (bits become the top half of a
+    binary32 word)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def plan_ref(rowptr, short_max: int, medium_max: int, chunk_nnz: int) -> dict:
+    """Row-binning plan, derived plainly on the CPU.
+
+    The pages motivate two ways to hand out the work of a row: one worker per
+    row, or the row's non-zeros divided among several workers ([Sgap], the
+    survey of prior work: Yang et al. choose between an nnz-balanced and a
+    row-split algorithm; the DA-SpMM points EB and RB).  [IntelMax] (SDDMM
+    implementation) divides the nnzr non-zeros of a row equally among NT
+    workers.  The plan below fixes that choice per row by its length:
+
+      len_i = rowptr[i+1] - rowptr[i]
+      short  : len_i <= short_max
+      medium : short_max < len_i <= medium_max
+      long   : len_i > medium_max, cut into n_i = ceil(len_i / chunk_nnz)
+               chunks; chunk k (0 <= k < n_i) covers positions
+               [rowptr[i] + floor(k*len_i/n_i), rowptr[i] + floor((k+1)*len_i/n_i)),
+               so the chunks tile the row in order and none exceeds chunk_nnz.
+
+    Lists are in ascending row order; chunks are ordered by row, then by k.
+    Returns a dict of int32 arrays:
+      medium_rows [n_medium]
+      long_rows   [n_long, 3]   (row, first chunk index, number of chunks)
+      chunks      [n_chunks, 4] (row, p0, p1, index of the row in long_rows)
+    plus the integer counts n_short, n_medium, n_long, n_chunks.
+    """
+    if not (0 <= short_max <= medium_max) or chunk_nnz < 1:
+        raise ValueError("need 0 <= short_max <= medium_max and chunk_nnz >= 1")
+    rp = np.asarray(rowptr, dtype=np.int64)
+    lengths = rp[1:] - rp[:-1]
+    is_short = lengths <= short_max
+    is_medium = (lengths > short_max) & (lengths <= medium_max)
+    is_long = lengths > medium_max
+    medium_rows = np.nonzero(is_medium)[0].astype(np.int32)
+    long_ids = np.nonzero(is_long)[0]
+    long_rows = []
+    chunks = []
+    for li, row in enumerate(long_ids):
+        start = int(rp[row])
+        length = int(lengths[row])
+        n = -(-length // chunk_nnz)
+        long_rows.append((int(row), len(chunks), n))
+        for k in range(n):
+            p0 = start + (k * length) // n
+            p1 = start + ((k + 1) * length) // n
+            chunks.append((int(row), p0, p1, li))
+    return {
+        "n_short": int(is_short.sum()),
+        "n_medium": int(medium_rows.shape[0]),
+        "n_long": len(long_rows),
+        "n_chunks": len(chunks),
+        "medium_rows": medium_rows,
+        "long_rows": np.array(long_rows, dtype=np.int32).reshape(-1, 3),
+        "chunks": np.array(chunks, dtype=np.int32).reshape(-1, 4),
+    }
