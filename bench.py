@@ -1,0 +1,235 @@
+"""Benchmark of the CSR sparse x dense product C = A*B on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one call of the library's entry point -- the planning pass and
+the worker kernel -- on the same resident inputs.  W untimed steps, then K
+timed steps bracketed by device synchronisation; rank 0 prints one JSON line.
+
+Metric: GFLOP/s = 2*nnz*N / time per step, with the effective bandwidth
+min_bytes / time, where min_bytes is the minimum HBM traffic of one product
+(rowptr, colind and vals read once, B read once, C written once).
+
+Besides the headline, the line carries
+  roofline      the worker kernel's algorithmic bytes (min_bytes) over its
+                mean duration, timed with HIP events that the library
+                records on the call's stream during the timed steps, against
+                the 8 TB/s HBM peak; `traffic` is the HBM bytes per launch
+                measured by rocprofv3 counters (FETCH_SIZE + WRITE_SIZE,
+                scaled by a copy kernel of known size) when the committed
+                profile matches the current kernel sources, else null;
+  cold          median and best of 20 event-timed calls, each after a 1 GiB
+                write that evicts L2 and the Infinity Cache;
+  cpu_baseline  the fp64 oracle timed on this host's cores on the same
+                matrix (a reported baseline, not a target).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("SpMM GFLOP/s (2·nnz·N) and effective HBM GB/s as % of peak, "
+          "1 MI355X")
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "powerlaw_262k_n64"
+KERNEL_SOURCES = ["sparse_dense_linear_amd/csrc/worker.hip",
+                  "sparse_dense_linear_amd/csrc/plan.hip",
+                  "sparse_dense_linear_amd/csrc/internal.h",
+                  "sparse_dense_linear_amd/csrc/api.hip"]
+COUNTER_FILE = os.path.join(ROOT, "profiles", "counters_{workload}.md")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def min_bytes(p) -> int:
+    """rowptr (M+1 int32) + colind and vals (nnz each) + B once + C (fp32)."""
+    s_val = p.vals.dtype.itemsize
+    s_b = p.B.dtype.itemsize
+    return 4 * (p.M + 1) + p.nnz * (4 + s_val) + p.K * p.N * s_b + 4 * p.M * p.N
+
+
+def flops(p) -> int:
+    return 2 * p.nnz * p.N
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per worker launch from the committed counter summary, if it
+    was taken on the current kernel sources."""
+    path = COUNTER_FILE.format(workload=workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"source_hash:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_src or not m_b or m_src.group(1) != kernel_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(p, budget_s: float = 10.0) -> dict:
+    import oracle
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.spmm_ref(p.rowptr, p.colind, p.vals, p.B, p.N, with_bound=False)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 1000:
+            break
+    return {"value": round(flops(p) * reps / el / 1e9, 4), "unit": "GFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the whole {p.name} matrix (C only, no bound), "
+                      f"{reps} repetitions in {el:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cold-reps", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import sparse_dense_linear_amd as sdl
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = 1 << 28  # 256 Mi floats = 1 GiB
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n,
+                          "launches": 5}))
+        return 0
+
+    p = W.make(args.workload)
+    rowptr = torch.from_numpy(p.rowptr).to(dev)
+    colind = torch.from_numpy(p.colind).to(dev)
+    if p.dtype == "f32":
+        vals = torch.from_numpy(p.vals).to(dev)
+        B = torch.from_numpy(p.B.reshape(-1)).to(dev)
+        fn = sdl.spmm_csr_f32
+    else:
+        vals = torch.from_numpy(p.vals.view(np.int16)).to(dev)
+        B = torch.from_numpy(p.B.reshape(-1).view(np.int16)).to(dev)
+        fn = sdl.spmm_csr_bf16in_f32acc
+    C = torch.empty(p.M * p.N, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fn(rowptr, colind, vals, B, C, p.M, p.K, p.N, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K back-to-back steps, HIP events around the worker kernel
+    sdl.timing_enable(True)
+    sdl.timing_read()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    sdl.timing_enable(False)
+    plan_ms, worker_ms, ncalls = sdl.timing_read()
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    gflops = flops(p) / (ms_per_step * 1e-3) / 1e9
+    mb = min_bytes(p)
+    eff = mb / (ms_per_step * 1e-3) / 1e9
+    worker_avg_ms = worker_ms / max(ncalls, 1)
+    plan_avg_ms = plan_ms / max(ncalls, 1)
+    achieved = mb / (worker_avg_ms * 1e-3) / 1e9 if worker_avg_ms > 0 else None
+
+    # cold calls: evict L2 and the Infinity Cache before each call
+    evict = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(args.cold_reps):
+        evict.fill_(1.0)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        e1.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del evict
+    cold_med = float(np.median(cold)) if cold else None
+
+    out = {
+        "metric": METRIC,
+        "value": round(gflops, 3),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if p.dtype == "f32" else "bf16-in/f32-acc",
+        "data": "synthetic",
+        "config": {"workload": p.name, "M": p.M, "K": p.K, "N": p.N,
+                   "nnz": p.nnz, **{k: v for k, v in p.meta.items()
+                                    if k not in ("hubs",)}},
+        "eff_GBps": round(eff, 2),
+        "hbm_frac": round(eff / HBM_PEAK_GBPS, 4),
+        "min_bytes": mb,
+        "flops_per_step": flops(p),
+        "kernel_ms": {"plan": round(plan_avg_ms, 6), "worker": round(worker_avg_ms, 6)},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": None if achieved is None else round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": None if achieved is None else round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(p.name),
+        },
+        "cold": {"median_ms": cold_med, "best_ms": min(cold) if cold else None,
+                 "reps": len(cold),
+                 "eff_GBps_median": None if not cold_med else round(mb / (cold_med * 1e-3) / 1e9, 2),
+                 "gflops_median": None if not cold_med else round(flops(p) / (cold_med * 1e-3) / 1e9, 3)},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,172 @@
+/*
+ * spmm.h -- C ABI of the MI355X (gfx950) CSR sparse x dense product library.
+ *
+ * Operation (page "Performance Optimization of Deep Learning Sparse Matrix
+ * Kernels on Intel Max Series GPU", the SpMM operation, Fig. 5 and
+ * Algorithm 2): given a sparse M x K matrix A in CSR form and a dense K x N
+ * matrix B, compute the dense M x N matrix
+ *
+ *     C[i, :] = sum over stored entries p of row i of  vals[p] * B[colind[p], :]
+ *
+ * i.e. every stored value scales one gathered row of B and is accumulated
+ * into its output row.  C is overwritten (it is computed, not updated):
+ * rows of A with no stored entries produce rows of +0.0.  Stored entries
+ * with the same column are all visited, so they add up.
+ *
+ * Layout
+ *   rowptr  int32[M+1]   absolute offsets into colind/vals; row i owns
+ *                        positions rowptr[i] .. rowptr[i+1]-1.  rowptr[0]
+ *                        may be non-zero, so a caller can pass a view of a
+ *                        block of rows (rowptr + r0, C + r0*N) without copies.
+ *   colind  int32[nnz]   column indices, 0 <= colind[p] < K; any order and
+ *                        repeats are allowed.
+ *   vals    [nnz]        float32, or bf16 bit patterns (uint16).
+ *   B       K x N        row-major, leading dimension exactly N.
+ *   C       M x N        float32, row-major, leading dimension exactly N.
+ *
+ * Ownership and memory: every pointer is device memory owned by the caller;
+ * the library never frees or retains it.  The library allocates its own
+ * scratch space (the row plan) from a stream-ordered pool per device, so
+ * calls on different streams do not share scratch.
+ *
+ * Asynchrony: a call only enqueues work on `stream` (a hipStream_t; NULL is
+ * the null stream) and returns; it never waits for the device.  Inputs must
+ * stay alive, and C must not be read, until the stream has passed the call.
+ *
+ * Errors: every call returns a status; nothing throws across the ABI.
+ * Argument errors are found on the host before any HIP call.  The contents
+ * of the CSR arrays are preconditions that the fast path does not check:
+ * rowptr must be non-decreasing, 0 <= colind < K, and
+ * rowptr[M] - rowptr[0] < 2^31.  spmm_last_error() gives a text for the most
+ * recent failure on the calling thread.
+ *
+ * Numerics: products and sums are carried in fp32 (bf16 inputs are widened
+ * exactly to fp32 first) with fused multiply-adds, in an order that differs
+ * from the sequential one.  Rows handled by one wavefront are bitwise
+ * repeatable from run to run; rows long enough to be split across
+ * wavefronts are reduced with fp32 atomic adds, whose order (and so the last
+ * bits) can differ between runs.
+ */
+#ifndef SDL_SPMM_H
+#define SDL_SPMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t spmm_status_t;
+
+#define SPMM_SUCCESS             0  /* work enqueued (or nothing to do)            */
+#define SPMM_ERROR_INVALID_VALUE 1  /* bad size, null pointer, bad option          */
+#define SPMM_ERROR_HIP           2  /* a HIP runtime call or a launch failed       */
+#define SPMM_ERROR_OUT_OF_MEMORY 3  /* the scratch space could not be allocated   */
+#define SPMM_ERROR_UNSUPPORTED   4  /* valid request this build does not serve    */
+
+#define SPMM_DTYPE_F32  0           /* vals and B are float32                    */
+#define SPMM_DTYPE_BF16 1           /* vals and B are bf16 bits, fp32 accumulate */
+
+/*
+ * Row-binning thresholds (the plan).  A row with len = rowptr[i+1]-rowptr[i]
+ * entries is
+ *   short   if len <= short_max          one sub-wavefront lane group per row
+ *   medium  if short_max < len <= medium_max   one wavefront per row
+ *   long    if len > medium_max          cut into ceil(len / chunk_nnz)
+ *                                        near-equal chunks, one wavefront each
+ * Fields < 0 (short_max, medium_max) or <= 0 (chunk_nnz) ask for the
+ * library's default for the given element type and N.  The thresholds never
+ * change C beyond rounding; they only route work.
+ */
+typedef struct spmm_tuning {
+    int32_t short_max;
+    int32_t medium_max;
+    int32_t chunk_nnz;
+    int32_t reserved;   /* must be 0 */
+} spmm_tuning_t;
+
+/*
+ * C = A * B with fp32 values and fp32 B, fp32 accumulation, fp32 C.
+ * M, K, N >= 0; M, K < 2^31.  M == 0 or N == 0: success, nothing launched.
+ * K == 0 requires an A with no stored entries (C becomes zero).
+ * Null pointers are rejected when the array they stand for is non-empty.
+ */
+spmm_status_t spmm_csr_f32(const int32_t *rowptr, const int32_t *colind,
+                           const float *vals, const float *B, float *C,
+                           int64_t M, int64_t K, int64_t N, void *stream);
+
+/*
+ * C = A * B with bf16 values and bf16 B (given as raw 16-bit patterns),
+ * widened exactly to fp32, fp32 accumulation, fp32 C.  Same rules as
+ * spmm_csr_f32.
+ */
+spmm_status_t spmm_csr_bf16in_f32acc(const int32_t *rowptr,
+                                     const int32_t *colind,
+                                     const uint16_t *vals, const uint16_t *B,
+                                     float *C, int64_t M, int64_t K,
+                                     int64_t N, void *stream);
+
+/*
+ * Either element type (dtype = SPMM_DTYPE_*) with explicit thresholds;
+ * tuning == NULL means all defaults.  Same rules as spmm_csr_f32, and a
+ * tuning with short_max > medium_max (after defaults) or reserved != 0 is
+ * SPMM_ERROR_INVALID_VALUE.
+ */
+spmm_status_t spmm_csr_tuned(int32_t dtype, const int32_t *rowptr,
+                             const int32_t *colind, const void *vals,
+                             const void *B, float *C, int64_t M, int64_t K,
+                             int64_t N, const spmm_tuning_t *tuning,
+                             void *stream);
+
+/*
+ * Host only, no HIP call: the thresholds a call with this dtype, N and
+ * requested tuning (NULL = all defaults) would use, written to *resolved.
+ */
+spmm_status_t spmm_resolve_tuning(int32_t dtype, int64_t N,
+                                  const spmm_tuning_t *requested,
+                                  spmm_tuning_t *resolved);
+
+/*
+ * Introspection for tests: run only the planning pass on device rowptr
+ * (M rows) with the given thresholds, wait for it, and copy the plan to
+ * host arrays:
+ *   counts[4]          n_short, n_medium, n_long, n_chunks
+ *   medium_rows[cap]   ascending rows with short_max < len <= medium_max
+ *   long_rows[3*cap]   per long row, ascending: row, first chunk, chunks
+ *   chunks[4*cap]      per chunk, ordered by row then position:
+ *                      row, first position, end position, long-row index
+ * Each output array receives at most `cap` records (counts are always
+ * complete).  Synchronises `stream`.  The chunk table the worker reads
+ * holds M + 4096 records; chunks beyond it are recomputed from long_rows,
+ * and this call reports the recomputed values for them as well.
+ */
+spmm_status_t spmm_plan_export(const int32_t *rowptr, int64_t M,
+                               const spmm_tuning_t *resolved, void *stream,
+                               int64_t cap, int64_t *counts,
+                               int32_t *medium_rows, int32_t *long_rows,
+                               int32_t *chunks);
+
+/* Static text naming a status code. */
+const char *spmm_status_string(spmm_status_t status);
+
+/* Text describing the most recent failure on the calling thread ("" if
+ * none).  Valid until the next library call on this thread. */
+const char *spmm_last_error(void);
+
+/*
+ * Kernel timing for benchmarks.  spmm_timing_enable(1) makes every later
+ * call record HIP events around its planning kernels and around its
+ * worker kernel on the call's stream; spmm_timing_read waits for the
+ * recorded events, returns the summed milliseconds and the number of calls
+ * timed, and clears the record.  Disabled by default; enabling adds two
+ * event records per call.
+ */
+spmm_status_t spmm_timing_enable(int32_t on);
+spmm_status_t spmm_timing_read(double *plan_ms, double *worker_ms,
+                               int64_t *calls);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDL_SPMM_H */

@@ -1,0 +1,472 @@
+// api.hip -- host side of the C ABI declared in include/spmm.h.
+//
+// Checks arguments before any HIP call, resolves the routing thresholds,
+// takes one call's scratch space (the row plan) from a stream-ordered pool,
+// enqueues the planning kernels and the worker kernel, and returns without
+// waiting for the device.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+#include "spmm.h"
+
+using namespace sdl;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+spmm_status_t fail(spmm_status_t st, const std::string &msg)
+{
+    g_last_error = msg;
+    return st;
+}
+
+spmm_status_t fail_hip(hipError_t err, const char *where)
+{
+    g_last_error = std::string(where) + ": " + hipGetErrorString(err);
+    return SPMM_ERROR_HIP;
+}
+
+constexpr int64_t kMaxIndex = (int64_t)1 << 31;  // int32 rows / columns
+
+// ----------------------------------------------------------- thresholds
+
+// Gathers a lane keeps in flight for a worker variant (see worker.hip).
+int unroll_of(int nv) { return nv == 1 ? 8 : (nv == 2 ? 4 : 2); }
+
+spmm_status_t resolve(int32_t dtype, int64_t N, const spmm_tuning_t *req,
+                      spmm_tuning_t *out)
+{
+    if (dtype != SPMM_DTYPE_F32 && dtype != SPMM_DTYPE_BF16)
+        return fail(SPMM_ERROR_INVALID_VALUE, "unknown dtype");
+    if (N < 0 || N >= kMaxIndex)
+        return fail(SPMM_ERROR_INVALID_VALUE, "N out of range");
+    if (req && req->reserved != 0)
+        return fail(SPMM_ERROR_INVALID_VALUE, "spmm_tuning_t.reserved must be 0");
+    // Nominal variant for this N (aligned pointers): R groups of G lanes.
+    const WorkerConfig cfg = choose_worker(dtype, N > 0 ? N : 1, nullptr, nullptr);
+    const int R = kWave / cfg.group;
+    const int U = unroll_of(cfg.nv);
+    // Defaults: a short row fits two unrolled gather rounds of one group;
+    // a wavefront item (medium row or long-row chunk) is about eight rounds
+    // of all R groups, kept within [256, 4096] entries.
+    int64_t chunk = (int64_t)R * U * 8;
+    chunk = chunk < 256 ? 256 : (chunk > 4096 ? 4096 : chunk);
+    spmm_tuning_t t;
+    t.short_max = 2 * U;
+    t.chunk_nnz = (int32_t)chunk;
+    t.medium_max = (int32_t)chunk;
+    t.reserved = 0;
+    if (req) {
+        if (req->short_max >= 0)
+            t.short_max = req->short_max;
+        if (req->medium_max >= 0)
+            t.medium_max = req->medium_max;
+        if (req->chunk_nnz > 0)
+            t.chunk_nnz = req->chunk_nnz;
+    }
+    if (t.short_max > t.medium_max)
+        return fail(SPMM_ERROR_INVALID_VALUE, "short_max > medium_max");
+    *out = t;
+    return SPMM_SUCCESS;
+}
+
+// ------------------------------------------------------------- scratch
+
+struct DevicePool {
+    bool ready = false;
+    hipMemPool_t pool = nullptr;
+};
+
+std::mutex g_pool_mu;
+std::vector<DevicePool> g_pools;
+
+hipError_t pool_for_device(int dev, hipMemPool_t *out)
+{
+    std::lock_guard<std::mutex> lock(g_pool_mu);
+    if ((int)g_pools.size() <= dev)
+        g_pools.resize(dev + 1);
+    DevicePool &p = g_pools[dev];
+    if (!p.ready) {
+        hipMemPoolProps props;
+        memset(&props, 0, sizeof props);
+        props.allocType = hipMemAllocationTypePinned;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipError_t err = hipMemPoolCreate(&p.pool, &props);
+        if (err != hipSuccess)
+            return err;
+        // Keep freed blocks cached in the pool instead of returning them to
+        // the device at every synchronisation.
+        uint64_t keep = UINT64_MAX;
+        err = hipMemPoolSetAttribute(p.pool, hipMemPoolAttrReleaseThreshold, &keep);
+        if (err != hipSuccess)
+            return err;
+        p.ready = true;
+    }
+    *out = p.pool;
+    return hipSuccess;
+}
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Byte offsets of the plan arrays inside one scratch block.
+struct ScratchLayout {
+    int64_t tile_counts, counts, medium_rows, long_rows, chunks, total;
+    int64_t chunk_cap;
+};
+
+ScratchLayout scratch_layout(int64_t M)
+{
+    const PlanShape s = plan_shape(M);
+    ScratchLayout l;
+    int64_t off = 0;
+    l.tile_counts = off;
+    off = align_up(off + 16 * s.n_tiles, 256);
+    l.counts = off;
+    off = align_up(off + (int64_t)sizeof(PlanCounts), 256);
+    l.medium_rows = off;
+    off = align_up(off + 4 * M, 256);
+    l.long_rows = off;
+    off = align_up(off + (int64_t)sizeof(LongRow) * M, 256);
+    l.chunk_cap = M + kChunkTableSlack;
+    l.chunks = off;
+    off = align_up(off + (int64_t)sizeof(Chunk) * l.chunk_cap, 256);
+    l.total = off;
+    return l;
+}
+
+PlanBuffers carve(char *base, const ScratchLayout &l)
+{
+    PlanBuffers b;
+    b.tile_counts = (int32_t *)(base + l.tile_counts);
+    b.counts = (PlanCounts *)(base + l.counts);
+    b.medium_rows = (int32_t *)(base + l.medium_rows);
+    b.long_rows = (LongRow *)(base + l.long_rows);
+    b.chunks = (Chunk *)(base + l.chunks);
+    b.chunk_cap = l.chunk_cap;
+    return b;
+}
+
+bool test_fail_alloc()
+{
+    const char *v = getenv("SPMM_TEST_FAIL_ALLOC");
+    return v != nullptr && v[0] == '1';
+}
+
+// --------------------------------------------------------------- timing
+
+struct TimedCall {
+    hipEvent_t e0, e1, e2;
+};
+
+std::mutex g_time_mu;
+bool g_timing = false;
+std::vector<TimedCall> g_timed;
+
+hipError_t record_event(hipEvent_t *ev, hipStream_t s)
+{
+    hipError_t err = hipEventCreate(ev);
+    if (err != hipSuccess)
+        return err;
+    return hipEventRecord(*ev, s);
+}
+
+// ---------------------------------------------------------------- calls
+
+spmm_status_t check_args(int32_t dtype, const int32_t *rowptr, const void *B,
+                         const float *C, int64_t M, int64_t K, int64_t N)
+{
+    if (dtype != SPMM_DTYPE_F32 && dtype != SPMM_DTYPE_BF16)
+        return fail(SPMM_ERROR_INVALID_VALUE, "unknown dtype");
+    if (M < 0 || K < 0 || N < 0)
+        return fail(SPMM_ERROR_INVALID_VALUE, "negative size");
+    if (M >= kMaxIndex || K >= kMaxIndex || N >= kMaxIndex)
+        return fail(SPMM_ERROR_INVALID_VALUE, "M, K and N must be below 2^31");
+    if (M == 0 || N == 0)
+        return SPMM_SUCCESS;
+    if (rowptr == nullptr)
+        return fail(SPMM_ERROR_INVALID_VALUE, "rowptr is null");
+    if (C == nullptr)
+        return fail(SPMM_ERROR_INVALID_VALUE, "C is null");
+    if (K > 0 && B == nullptr)
+        return fail(SPMM_ERROR_INVALID_VALUE, "B is null");
+    if (((uintptr_t)C) % 4 != 0)
+        return fail(SPMM_ERROR_INVALID_VALUE, "C is not 4-byte aligned");
+    const uintptr_t esz = dtype == SPMM_DTYPE_BF16 ? 2 : 4;
+    if (((uintptr_t)B) % esz != 0)
+        return fail(SPMM_ERROR_INVALID_VALUE, "B is not aligned to its element size");
+    return SPMM_SUCCESS;
+}
+
+spmm_status_t run(int32_t dtype, const int32_t *rowptr, const int32_t *colind,
+                  const void *vals, const void *B, float *C, int64_t M,
+                  int64_t K, int64_t N, const spmm_tuning_t *tuning,
+                  void *stream_ptr)
+{
+    g_last_error.clear();
+    spmm_status_t st = check_args(dtype, rowptr, B, C, M, K, N);
+    if (st != SPMM_SUCCESS)
+        return st;
+    spmm_tuning_t t;
+    st = resolve(dtype, N, tuning, &t);
+    if (st != SPMM_SUCCESS)
+        return st;
+    if (M == 0 || N == 0)
+        return SPMM_SUCCESS;
+    if (test_fail_alloc())
+        return fail(SPMM_ERROR_OUT_OF_MEMORY, "allocation failure forced by SPMM_TEST_FAIL_ALLOC");
+
+    hipStream_t stream = (hipStream_t)stream_ptr;
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return fail_hip(err, "hipGetDevice");
+    hipMemPool_t pool;
+    err = pool_for_device(dev, &pool);
+    if (err != hipSuccess)
+        return fail_hip(err, "hipMemPoolCreate");
+    const ScratchLayout lay = scratch_layout(M);
+    void *scratch = nullptr;
+    err = hipMallocFromPoolAsync(&scratch, (size_t)lay.total, pool, stream);
+    if (err == hipErrorOutOfMemory || (err == hipSuccess && scratch == nullptr))
+        return fail(SPMM_ERROR_OUT_OF_MEMORY, "scratch allocation failed");
+    if (err != hipSuccess)
+        return fail_hip(err, "hipMallocFromPoolAsync");
+
+    const PlanBuffers pb = carve((char *)scratch, lay);
+    Thresholds th;
+    th.short_max = t.short_max;
+    th.medium_max = t.medium_max;
+    th.chunk_nnz = t.chunk_nnz;
+
+    bool timing;
+    {
+        std::lock_guard<std::mutex> lock(g_time_mu);
+        timing = g_timing;
+    }
+    TimedCall tc{};
+    if (timing && (err = record_event(&tc.e0, stream)) != hipSuccess)
+        return fail_hip(err, "hipEventRecord");
+
+    err = launch_plan(rowptr, M, th, pb, C, N, stream);
+    if (err != hipSuccess) {
+        hipFreeAsync(scratch, stream);
+        return fail_hip(err, "plan kernels");
+    }
+    if (timing && (err = record_event(&tc.e1, stream)) != hipSuccess)
+        return fail_hip(err, "hipEventRecord");
+
+    WorkerArgs wa;
+    wa.rowptr = rowptr;
+    wa.colind = colind;
+    wa.vals = vals;
+    wa.B = B;
+    wa.C = C;
+    wa.M = M;
+    wa.N = N;
+    wa.th = th;
+    wa.plan = pb;
+    const WorkerConfig cfg = choose_worker(dtype, N, B, C);
+    err = launch_worker(cfg, wa, stream);
+    if (err != hipSuccess) {
+        hipFreeAsync(scratch, stream);
+        return fail_hip(err, "worker kernel");
+    }
+    if (timing) {
+        if ((err = record_event(&tc.e2, stream)) != hipSuccess)
+            return fail_hip(err, "hipEventRecord");
+        std::lock_guard<std::mutex> lock(g_time_mu);
+        g_timed.push_back(tc);
+    }
+    err = hipFreeAsync(scratch, stream);
+    if (err != hipSuccess)
+        return fail_hip(err, "hipFreeAsync");
+    return SPMM_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+spmm_status_t spmm_csr_f32(const int32_t *rowptr, const int32_t *colind,
+                           const float *vals, const float *B, float *C,
+                           int64_t M, int64_t K, int64_t N, void *stream)
+{
+    return run(SPMM_DTYPE_F32, rowptr, colind, vals, B, C, M, K, N, nullptr,
+               stream);
+}
+
+spmm_status_t spmm_csr_bf16in_f32acc(const int32_t *rowptr,
+                                     const int32_t *colind,
+                                     const uint16_t *vals, const uint16_t *B,
+                                     float *C, int64_t M, int64_t K,
+                                     int64_t N, void *stream)
+{
+    return run(SPMM_DTYPE_BF16, rowptr, colind, vals, B, C, M, K, N, nullptr,
+               stream);
+}
+
+spmm_status_t spmm_csr_tuned(int32_t dtype, const int32_t *rowptr,
+                             const int32_t *colind, const void *vals,
+                             const void *B, float *C, int64_t M, int64_t K,
+                             int64_t N, const spmm_tuning_t *tuning,
+                             void *stream)
+{
+    return run(dtype, rowptr, colind, vals, B, C, M, K, N, tuning, stream);
+}
+
+spmm_status_t spmm_resolve_tuning(int32_t dtype, int64_t N,
+                                  const spmm_tuning_t *requested,
+                                  spmm_tuning_t *resolved)
+{
+    g_last_error.clear();
+    if (resolved == nullptr)
+        return fail(SPMM_ERROR_INVALID_VALUE, "resolved is null");
+    return resolve(dtype, N, requested, resolved);
+}
+
+spmm_status_t spmm_plan_export(const int32_t *rowptr, int64_t M,
+                               const spmm_tuning_t *resolved, void *stream_ptr,
+                               int64_t cap, int64_t *counts,
+                               int32_t *medium_rows, int32_t *long_rows,
+                               int32_t *chunks)
+{
+    g_last_error.clear();
+    if (resolved == nullptr || counts == nullptr)
+        return fail(SPMM_ERROR_INVALID_VALUE, "null argument");
+    if (resolved->short_max < 0 || resolved->medium_max < resolved->short_max ||
+        resolved->chunk_nnz <= 0 || resolved->reserved != 0)
+        return fail(SPMM_ERROR_INVALID_VALUE, "tuning must be fully resolved");
+    if (M < 0 || M >= kMaxIndex || cap < 0)
+        return fail(SPMM_ERROR_INVALID_VALUE, "M or cap out of range");
+    if (cap > 0 && (medium_rows == nullptr || long_rows == nullptr || chunks == nullptr))
+        return fail(SPMM_ERROR_INVALID_VALUE, "null output array");
+    for (int q = 0; q < 4; ++q)
+        counts[q] = 0;
+    if (M == 0)
+        return SPMM_SUCCESS;
+    if (rowptr == nullptr)
+        return fail(SPMM_ERROR_INVALID_VALUE, "rowptr is null");
+
+    hipStream_t stream = (hipStream_t)stream_ptr;
+    const ScratchLayout lay = scratch_layout(M);
+    void *scratch = nullptr;
+    hipError_t err = hipMalloc(&scratch, (size_t)lay.total);
+    if (err != hipSuccess)
+        return fail_hip(err, "hipMalloc");
+    const PlanBuffers pb = carve((char *)scratch, lay);
+    Thresholds th;
+    th.short_max = resolved->short_max;
+    th.medium_max = resolved->medium_max;
+    th.chunk_nnz = resolved->chunk_nnz;
+    Chunk *expanded = nullptr;
+    spmm_status_t st = SPMM_SUCCESS;
+    PlanCounts pc;
+    do {
+        if ((err = launch_plan(rowptr, M, th, pb, nullptr, 0, stream)) != hipSuccess ||
+            (err = hipMemcpyAsync(&pc, pb.counts, sizeof pc, hipMemcpyDeviceToHost,
+                                  stream)) != hipSuccess ||
+            (err = hipStreamSynchronize(stream)) != hipSuccess) {
+            st = fail_hip(err, "plan");
+            break;
+        }
+        counts[0] = pc.n_short;
+        counts[1] = pc.n_medium;
+        counts[2] = pc.n_long;
+        counts[3] = pc.n_chunks;
+        const int64_t nm = pc.n_medium < cap ? pc.n_medium : cap;
+        const int64_t nl = pc.n_long < cap ? pc.n_long : cap;
+        const int64_t nc = pc.n_chunks < cap ? pc.n_chunks : cap;
+        if (nm > 0 && (err = hipMemcpy(medium_rows, pb.medium_rows, 4 * nm,
+                                       hipMemcpyDeviceToHost)) != hipSuccess) {
+            st = fail_hip(err, "copy medium rows");
+            break;
+        }
+        if (nl > 0 && (err = hipMemcpy(long_rows, pb.long_rows, sizeof(LongRow) * nl,
+                                       hipMemcpyDeviceToHost)) != hipSuccess) {
+            st = fail_hip(err, "copy long rows");
+            break;
+        }
+        if (nc > 0) {
+            if ((err = hipMalloc(&expanded, sizeof(Chunk) * nc)) != hipSuccess ||
+                (err = launch_chunk_expand(rowptr, th, pb, nc, expanded, stream)) != hipSuccess ||
+                (err = hipStreamSynchronize(stream)) != hipSuccess ||
+                (err = hipMemcpy(chunks, expanded, sizeof(Chunk) * nc,
+                                 hipMemcpyDeviceToHost)) != hipSuccess) {
+                st = fail_hip(err, "expand chunks");
+                break;
+            }
+        }
+    } while (0);
+    if (expanded)
+        hipFree(expanded);
+    hipFree(scratch);
+    return st;
+}
+
+const char *spmm_status_string(spmm_status_t status)
+{
+    switch (status) {
+    case SPMM_SUCCESS: return "SPMM_SUCCESS";
+    case SPMM_ERROR_INVALID_VALUE: return "SPMM_ERROR_INVALID_VALUE";
+    case SPMM_ERROR_HIP: return "SPMM_ERROR_HIP";
+    case SPMM_ERROR_OUT_OF_MEMORY: return "SPMM_ERROR_OUT_OF_MEMORY";
+    case SPMM_ERROR_UNSUPPORTED: return "SPMM_ERROR_UNSUPPORTED";
+    default: return "SPMM_ERROR_UNKNOWN";
+    }
+}
+
+const char *spmm_last_error(void) { return g_last_error.c_str(); }
+
+spmm_status_t spmm_timing_enable(int32_t on)
+{
+    std::lock_guard<std::mutex> lock(g_time_mu);
+    g_timing = on != 0;
+    return SPMM_SUCCESS;
+}
+
+spmm_status_t spmm_timing_read(double *plan_ms, double *worker_ms,
+                               int64_t *calls)
+{
+    g_last_error.clear();
+    std::vector<TimedCall> taken;
+    {
+        std::lock_guard<std::mutex> lock(g_time_mu);
+        taken.swap(g_timed);
+    }
+    double p = 0.0, w = 0.0;
+    spmm_status_t st = SPMM_SUCCESS;
+    for (const TimedCall &tc : taken) {
+        float a = 0.0f, b = 0.0f;
+        hipError_t err = hipEventSynchronize(tc.e2);
+        if (err == hipSuccess)
+            err = hipEventElapsedTime(&a, tc.e0, tc.e1);
+        if (err == hipSuccess)
+            err = hipEventElapsedTime(&b, tc.e1, tc.e2);
+        if (err != hipSuccess && st == SPMM_SUCCESS)
+            st = fail_hip(err, "hipEventElapsedTime");
+        p += a;
+        w += b;
+        hipEventDestroy(tc.e0);
+        hipEventDestroy(tc.e1);
+        hipEventDestroy(tc.e2);
+    }
+    if (plan_ms)
+        *plan_ms = p;
+    if (worker_ms)
+        *worker_ms = w;
+    if (calls)
+        *calls = (int64_t)taken.size();
+    return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+"""Shared helpers of the GPU parity tests: upload a problem, run the HIP
+library through the binding, compare with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import sparse_dense_linear_amd as sdl
+
+#: Per-element bound |C_gpu - C_ref| <= TOL * S + 1e-6 (S = |A||B|).
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+ABS = 1e-6
+
+
+def dev_arrays(p, device="cuda"):
+    rowptr = torch.from_numpy(p.rowptr).to(device)
+    colind = torch.from_numpy(p.colind).to(device)
+    if p.dtype == "f32":
+        vals = torch.from_numpy(p.vals).to(device)
+        B = torch.from_numpy(np.ascontiguousarray(p.B).reshape(-1)).to(device)
+    else:
+        vals = torch.from_numpy(p.vals.view(np.int16)).to(device)
+        B = torch.from_numpy(np.ascontiguousarray(p.B).reshape(-1).view(np.int16)).to(device)
+    return rowptr, colind, vals, B
+
+
+def call(p, rowptr, colind, vals, B, C, M=None, tuning=None):
+    M = p.M if M is None else M
+    if tuning is not None:
+        dt = sdl.DTYPE_F32 if p.dtype == "f32" else sdl.DTYPE_BF16
+        sdl.spmm_csr_tuned(dt, rowptr, colind, vals, B, C, M, p.K, p.N, tuning)
+    elif p.dtype == "f32":
+        sdl.spmm_csr_f32(rowptr, colind, vals, B, C, M, p.K, p.N)
+    else:
+        sdl.spmm_csr_bf16in_f32acc(rowptr, colind, vals, B, C, M, p.K, p.N)
+
+
+def run_gpu(p, tuning=None, fill=float("nan")):
+    """C from the HIP library; C starts filled with `fill` (NaN by default),
+    so any element the library fails to write is caught."""
+    rowptr, colind, vals, B = dev_arrays(p)
+    C = torch.full((p.M * p.N,), fill, dtype=torch.float32, device="cuda")
+    call(p, rowptr, colind, vals, B, C, tuning=tuning)
+    torch.cuda.synchronize()
+    return C.cpu().numpy().reshape(p.M, p.N)
+
+
+def reference(p, rows=None):
+    return oracle.spmm_ref(p.rowptr, p.colind, p.vals, p.B, p.N, rows=rows)
+
+
+def assert_parity(C, Cref, Sref, dtype, what=""):
+    C = np.asarray(C, dtype=np.float64)
+    err = np.abs(C - Cref)
+    lim = TOL[dtype] * Sref + ABS
+    bad = ~(err <= lim)          # NaN counts as a failure
+    if bad.any():
+        idx = np.argwhere(bad)
+        i, n = idx[0]
+        raise AssertionError(
+            f"{what}: {int(bad.sum())} of {bad.size} elements outside the bound; "
+            f"first at ({i},{n}): gpu={C[i, n]!r} ref={Cref[i, n]!r} "
+            f"S={Sref[i, n]!r}")
+    return float((err / np.maximum(Sref, 1e-30)).max()) if err.size else 0.0

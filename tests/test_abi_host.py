@@ -1,0 +1,159 @@
+"""The C-ABI library without a GPU: it loads, exports every function the
+header declares, resolves thresholds, and rejects bad arguments on the host
+before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import sparse_dense_linear_amd as sdl
+from sparse_dense_linear_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spmm.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spmm_\w+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    names = header_functions()
+    for must in ("spmm_csr_f32", "spmm_csr_bf16in_f32acc", "spmm_csr_tuned",
+                 "spmm_resolve_tuning", "spmm_plan_export", "spmm_status_string",
+                 "spmm_last_error", "spmm_timing_enable", "spmm_timing_read"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(sdl.lib_path())
+    missing = [n for n in header_functions() if not hasattr(lib, n)]
+    assert not missing, f"not exported: {missing}"
+
+
+def test_status_strings():
+    assert sdl.status_string(0) == "SPMM_SUCCESS"
+    assert sdl.status_string(1) == "SPMM_ERROR_INVALID_VALUE"
+    assert sdl.status_string(2) == "SPMM_ERROR_HIP"
+    assert sdl.status_string(3) == "SPMM_ERROR_OUT_OF_MEMORY"
+    assert sdl.status_string(4) == "SPMM_ERROR_UNSUPPORTED"
+    assert sdl.status_string(99) == "SPMM_ERROR_UNKNOWN"
+
+
+@pytest.mark.parametrize("dtype,N", [(0, 32), (0, 64), (0, 128), (0, 1), (0, 1000),
+                                     (1, 256), (1, 512), (1, 3)])
+def test_resolve_defaults_are_consistent(dtype, N):
+    t = sdl.resolve_tuning(dtype, N)
+    assert 0 <= t.short_max <= t.medium_max
+    assert 256 <= t.chunk_nnz <= 4096
+    # explicit values win over defaults
+    u = sdl.resolve_tuning(dtype, N, sdl.Tuning(3, 77, 11))
+    assert (u.short_max, u.medium_max, u.chunk_nnz) == (3, 77, 11)
+
+
+def test_resolve_rejects_bad_input():
+    with pytest.raises(sdl.SpmmError) as e:
+        sdl.resolve_tuning(0, 64, sdl.Tuning(10, 5, 4))
+    assert e.value.status == 1
+    with pytest.raises(sdl.SpmmError):
+        sdl.resolve_tuning(7, 64)
+    with pytest.raises(sdl.SpmmError):
+        sdl.resolve_tuning(0, -1)
+
+
+def raw_call(fn, *args):
+    L = sdl.lib()
+    return getattr(L, fn)(*args)
+
+
+FAKE = 0x10000  # never dereferenced: every case below fails or returns first
+
+
+@pytest.mark.parametrize("M,K,N,rowptr,B,C,expect", [
+    (-1, 4, 4, FAKE, FAKE, FAKE, 1),        # negative M
+    (4, -1, 4, FAKE, FAKE, FAKE, 1),        # negative K
+    (4, 4, -2, FAKE, FAKE, FAKE, 1),        # negative N
+    (2 ** 31, 4, 4, FAKE, FAKE, FAKE, 1),   # M too large for int32 rows
+    (4, 2 ** 31, 4, FAKE, FAKE, FAKE, 1),   # K too large
+    (4, 4, 4, None, FAKE, FAKE, 1),         # rowptr null
+    (4, 4, 4, FAKE, None, FAKE, 1),         # B null with K > 0
+    (4, 4, 4, FAKE, FAKE, None, 1),         # C null
+    (4, 4, 4, FAKE, FAKE, FAKE + 2, 1),     # C misaligned
+    (4, 4, 4, FAKE, FAKE + 1, FAKE, 1),     # B misaligned for fp32
+    (0, 4, 4, None, None, None, 0),         # M == 0: nothing to do
+    (4, 4, 0, None, None, None, 0),         # N == 0: nothing to do
+])
+def test_host_validation_f32(M, K, N, rowptr, B, C, expect):
+    rc = raw_call("spmm_csr_f32", rowptr, FAKE, FAKE, B, C, M, K, N, None)
+    assert rc == expect, sdl.lib().spmm_last_error()
+
+
+def test_host_validation_bf16_alignment():
+    # bf16 B needs 2-byte alignment only; an odd address is rejected
+    rc = raw_call("spmm_csr_bf16in_f32acc", FAKE, FAKE, FAKE, FAKE + 1, FAKE,
+                  4, 4, 4, None)
+    assert rc == 1
+
+
+def test_tuned_rejects_bad_tuning():
+    bad = _binding._TuningStruct(10, 5, 4, 0)
+    rc = raw_call("spmm_csr_tuned", 0, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 4,
+                  ctypes.byref(bad), None)
+    assert rc == 1
+    reserved = _binding._TuningStruct(1, 5, 4, 1)
+    rc = raw_call("spmm_csr_tuned", 0, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 4,
+                  ctypes.byref(reserved), None)
+    assert rc == 1
+    rc = raw_call("spmm_csr_tuned", 5, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 4,
+                  None, None)
+    assert rc == 1
+
+
+def test_forced_allocation_failure(monkeypatch):
+    monkeypatch.setenv("SPMM_TEST_FAIL_ALLOC", "1")
+    rc = raw_call("spmm_csr_f32", FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 4, None)
+    assert rc == 3
+    assert b"SPMM_TEST_FAIL_ALLOC" in sdl.lib().spmm_last_error()
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
+def test_valid_call_without_gpu_reports_hip_error():
+    rc = raw_call("spmm_csr_f32", FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 4, None)
+    assert rc == 2
+    assert sdl.lib().spmm_last_error() != b""
+
+
+def test_plan_export_validation():
+    counts = (ctypes.c_int64 * 4)()
+    t = _binding._TuningStruct(-1, 5, 4, 0)   # not resolved
+    rc = raw_call("spmm_plan_export", FAKE, 4, ctypes.byref(t), None, 0, counts,
+                  None, None, None)
+    assert rc == 1
+    t = _binding._TuningStruct(1, 5, 4, 0)
+    rc = raw_call("spmm_plan_export", FAKE, 0, ctypes.byref(t), None, 0, counts,
+                  None, None, None)
+    assert rc == 0 and list(counts) == [0, 0, 0, 0]
+
+
+def test_timing_read_empty():
+    sdl.timing_enable(False)
+    assert sdl.timing_read() == (0.0, 0.0, 0)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "_LIB_FILE", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _binding.lib()
+
+
+def test_binding_checks_operands():
+    """Marshalling rejects CPU tensors and wrong dtypes before any call."""
+    t = torch.zeros(4, dtype=torch.int32)
+    f = torch.zeros(4, dtype=torch.float32)
+    with pytest.raises((ValueError, TypeError)):
+        sdl.spmm_csr_f32(t, t, f, f, f, 3, 2, 2)

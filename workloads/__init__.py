@@ -135,6 +135,8 @@ def _distinct_sorted_variable(rng, lengths, K) -> np.ndarray:
     M = lengths.shape[0]
     if np.any(lengths > K):
         raise ValueError("a row is longer than K")
+    if not lengths.any():
+        return np.zeros(0, dtype=np.int64)
     rows = np.repeat(np.arange(M, dtype=np.int64), lengths)
     keys = np.unique(rows * K + rng.integers(0, K, size=rows.shape[0]))
     while True:
@@ -322,3 +324,16 @@ def make(name: str) -> CsrProblem:
     """Build one of the full-size workloads by name."""
     return WORKLOADS[name]()
 
+
+
+def rows_with_lengths(lengths, K, N, seed=0, dtype="f32", name="lengths",
+                      value_range=(-1.0, 1.0)) -> CsrProblem:
+    """Edge-case problem with the given row lengths: uniform distinct sorted
+    columns in [0, K), vals U(value_range), B U(-1,1)."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    M = lengths.shape[0]
+    rng = np.random.default_rng(seed)
+    cols = _distinct_sorted_variable(rng, lengths, K)
+    vals = _uniform_f32(rng, cols.shape[0], *value_range)
+    B = _uniform_f32(rng, K * N, -1.0, 1.0)
+    return _finish(name, M, K, N, lengths, cols, vals, B, dtype, {"seed": seed})
