@@ -4,6 +4,7 @@
 // takes one call's scratch space (the row plan) from a stream-ordered pool,
 // enqueues the planning kernels and the worker kernel, and returns without
 // waiting for the device.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -73,6 +74,11 @@ spmm_status_t resolve(int32_t dtype, int64_t N, const spmm_tuning_t *req,
         if (req->chunk_nnz > 0)
             t.chunk_nnz = req->chunk_nnz;
     }
+    // A short tile stages at most kShortCap entries and holds at least R
+    // rows, so a short row may hold at most kShortCap / R entries; longer
+    // rows go to the medium kind.
+    if (t.short_max > kShortCap / R)
+        t.short_max = kShortCap / R;
     if (t.short_max > t.medium_max)
         return fail(SPMM_ERROR_INVALID_VALUE, "short_max > medium_max");
     *out = t;
@@ -162,22 +168,77 @@ bool test_fail_alloc()
     return v != nullptr && v[0] == '1';
 }
 
+// Scratch space is kept per (device, stream) and reused by later calls on
+// the same stream, which stream order serialises; it grows (allocate the
+// larger block, free the old one, both stream-ordered) when a call needs
+// more.  Calls on different streams never share scratch.
+struct StreamScratch {
+    int dev;
+    hipStream_t stream;
+    void *ptr;
+    size_t size;
+};
+
+std::mutex g_scratch_mu;
+std::vector<StreamScratch> g_scratch;
+
+hipError_t scratch_for(int dev, hipStream_t stream, size_t need, void **out)
+{
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    StreamScratch *slot = nullptr;
+    for (StreamScratch &e : g_scratch)
+        if (e.dev == dev && e.stream == stream)
+            slot = &e;
+    if (slot && slot->size >= need) {
+        *out = slot->ptr;
+        return hipSuccess;
+    }
+    hipMemPool_t pool;
+    hipError_t err = pool_for_device(dev, &pool);
+    if (err != hipSuccess)
+        return err;
+    size_t size = need;
+    if (slot && size < slot->size + slot->size / 4)
+        size = slot->size + slot->size / 4;
+    void *ptr = nullptr;
+    err = hipMallocFromPoolAsync(&ptr, size, pool, stream);
+    if (err != hipSuccess)
+        return err;
+    if (ptr == nullptr)
+        return hipErrorOutOfMemory;
+    if (slot) {
+        hipFreeAsync(slot->ptr, stream);
+        slot->ptr = ptr;
+        slot->size = size;
+    } else {
+        g_scratch.push_back(StreamScratch{dev, stream, ptr, size});
+    }
+    *out = ptr;
+    return hipSuccess;
+}
+
 // --------------------------------------------------------------- timing
 
+// Kernel timing: the start/stop events are attached to the kernel dispatch
+// packets themselves (hipExtLaunchKernel), so timing adds no packets to the
+// stream.  Events are recycled through a free list.
 struct TimedCall {
-    hipEvent_t e0, e1, e2;
+    hipEvent_t plan0, plan1, work0, work1;
 };
 
 std::mutex g_time_mu;
 bool g_timing = false;
 std::vector<TimedCall> g_timed;
+std::vector<hipEvent_t> g_free_events;
 
-hipError_t record_event(hipEvent_t *ev, hipStream_t s)
+hipError_t take_event(hipEvent_t *ev)
 {
-    hipError_t err = hipEventCreate(ev);
-    if (err != hipSuccess)
-        return err;
-    return hipEventRecord(*ev, s);
+    if (!g_free_events.empty()) {
+        *ev = g_free_events.back();
+        g_free_events.pop_back();
+        return hipSuccess;
+    }
+    return hipEventCreate(ev);
 }
 
 // ---------------------------------------------------------------- calls
@@ -204,6 +265,9 @@ spmm_status_t check_args(int32_t dtype, const int32_t *rowptr, const void *B,
     const uintptr_t esz = dtype == SPMM_DTYPE_BF16 ? 2 : 4;
     if (((uintptr_t)B) % esz != 0)
         return fail(SPMM_ERROR_INVALID_VALUE, "B is not aligned to its element size");
+    // The kernels address a row of B with a 32-bit byte stride.
+    if ((uint64_t)N * esz > 0xFFFFFFFFull)
+        return fail(SPMM_ERROR_UNSUPPORTED, "a row of B must be below 4 GiB");
     return SPMM_SUCCESS;
 }
 
@@ -230,17 +294,13 @@ spmm_status_t run(int32_t dtype, const int32_t *rowptr, const int32_t *colind,
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess)
         return fail_hip(err, "hipGetDevice");
-    hipMemPool_t pool;
-    err = pool_for_device(dev, &pool);
-    if (err != hipSuccess)
-        return fail_hip(err, "hipMemPoolCreate");
     const ScratchLayout lay = scratch_layout(M);
     void *scratch = nullptr;
-    err = hipMallocFromPoolAsync(&scratch, (size_t)lay.total, pool, stream);
-    if (err == hipErrorOutOfMemory || (err == hipSuccess && scratch == nullptr))
+    err = scratch_for(dev, stream, (size_t)lay.total, &scratch);
+    if (err == hipErrorOutOfMemory)
         return fail(SPMM_ERROR_OUT_OF_MEMORY, "scratch allocation failed");
     if (err != hipSuccess)
-        return fail_hip(err, "hipMallocFromPoolAsync");
+        return fail_hip(err, "scratch allocation");
 
     const PlanBuffers pb = carve((char *)scratch, lay);
     Thresholds th;
@@ -248,22 +308,22 @@ spmm_status_t run(int32_t dtype, const int32_t *rowptr, const int32_t *colind,
     th.medium_max = t.medium_max;
     th.chunk_nnz = t.chunk_nnz;
 
+    TimedCall tc{};
     bool timing;
     {
         std::lock_guard<std::mutex> lock(g_time_mu);
         timing = g_timing;
+        if (timing &&
+            ((err = take_event(&tc.plan0)) != hipSuccess ||
+             (err = take_event(&tc.plan1)) != hipSuccess ||
+             (err = take_event(&tc.work0)) != hipSuccess ||
+             (err = take_event(&tc.work1)) != hipSuccess))
+            return fail_hip(err, "hipEventCreate");
     }
-    TimedCall tc{};
-    if (timing && (err = record_event(&tc.e0, stream)) != hipSuccess)
-        return fail_hip(err, "hipEventRecord");
 
-    err = launch_plan(rowptr, M, th, pb, C, N, stream);
-    if (err != hipSuccess) {
-        hipFreeAsync(scratch, stream);
+    err = launch_plan(rowptr, M, th, pb, C, N, stream, tc.plan0, tc.plan1);
+    if (err != hipSuccess)
         return fail_hip(err, "plan kernels");
-    }
-    if (timing && (err = record_event(&tc.e1, stream)) != hipSuccess)
-        return fail_hip(err, "hipEventRecord");
 
     WorkerArgs wa;
     wa.rowptr = rowptr;
@@ -272,24 +332,18 @@ spmm_status_t run(int32_t dtype, const int32_t *rowptr, const int32_t *colind,
     wa.B = B;
     wa.C = C;
     wa.M = M;
+    wa.K = K;
     wa.N = N;
     wa.th = th;
     wa.plan = pb;
     const WorkerConfig cfg = choose_worker(dtype, N, B, C);
-    err = launch_worker(cfg, wa, stream);
-    if (err != hipSuccess) {
-        hipFreeAsync(scratch, stream);
+    err = launch_worker(cfg, wa, stream, tc.work0, tc.work1);
+    if (err != hipSuccess)
         return fail_hip(err, "worker kernel");
-    }
     if (timing) {
-        if ((err = record_event(&tc.e2, stream)) != hipSuccess)
-            return fail_hip(err, "hipEventRecord");
         std::lock_guard<std::mutex> lock(g_time_mu);
         g_timed.push_back(tc);
     }
-    err = hipFreeAsync(scratch, stream);
-    if (err != hipSuccess)
-        return fail_hip(err, "hipFreeAsync");
     return SPMM_SUCCESS;
 }
 
@@ -372,7 +426,7 @@ spmm_status_t spmm_plan_export(const int32_t *rowptr, int64_t M,
     spmm_status_t st = SPMM_SUCCESS;
     PlanCounts pc;
     do {
-        if ((err = launch_plan(rowptr, M, th, pb, nullptr, 0, stream)) != hipSuccess ||
+        if ((err = launch_plan(rowptr, M, th, pb, nullptr, 0, stream, nullptr, nullptr)) != hipSuccess ||
             (err = hipMemcpyAsync(&pc, pb.counts, sizeof pc, hipMemcpyDeviceToHost,
                                   stream)) != hipSuccess ||
             (err = hipStreamSynchronize(stream)) != hipSuccess) {
@@ -447,18 +501,24 @@ spmm_status_t spmm_timing_read(double *plan_ms, double *worker_ms,
     spmm_status_t st = SPMM_SUCCESS;
     for (const TimedCall &tc : taken) {
         float a = 0.0f, b = 0.0f;
-        hipError_t err = hipEventSynchronize(tc.e2);
+        hipError_t err = hipEventSynchronize(tc.work1);
         if (err == hipSuccess)
-            err = hipEventElapsedTime(&a, tc.e0, tc.e1);
+            err = hipEventElapsedTime(&a, tc.plan0, tc.plan1);
         if (err == hipSuccess)
-            err = hipEventElapsedTime(&b, tc.e1, tc.e2);
+            err = hipEventElapsedTime(&b, tc.work0, tc.work1);
         if (err != hipSuccess && st == SPMM_SUCCESS)
             st = fail_hip(err, "hipEventElapsedTime");
         p += a;
         w += b;
-        hipEventDestroy(tc.e0);
-        hipEventDestroy(tc.e1);
-        hipEventDestroy(tc.e2);
+    }
+    {
+        std::lock_guard<std::mutex> lock(g_time_mu);
+        for (const TimedCall &tc : taken) {
+            g_free_events.push_back(tc.plan0);
+            g_free_events.push_back(tc.plan1);
+            g_free_events.push_back(tc.work0);
+            g_free_events.push_back(tc.work1);
+        }
     }
     if (plan_ms)
         *plan_ms = p;

@@ -13,6 +13,10 @@ constexpr int kBlock = kWave * kWavesPerBlock;
 constexpr int kPlanBlock = 256;      // planning kernels: threads per block
 constexpr int kPlanMaxTiles = 2048;  // planning tiles per call (upper bound)
 constexpr int64_t kChunkTableSlack = 4096;  // chunk table holds M + this
+// Entries of one short tile staged per wavefront; short_max is capped at
+// kShortCap / R (R = row groups per wavefront) so that a tile of at least R
+// rows always fits.
+constexpr int kShortCap = 512;
 
 // Routing thresholds, already resolved (see spmm_tuning_t).
 struct Thresholds {
@@ -65,9 +69,10 @@ PlanShape plan_shape(int64_t M);
 
 // Enqueue the two planning kernels.  When zero_long_rows is set, the C rows
 // of long rows (leading dimension N) are cleared for atomic accumulation.
+// start/stop (may be null) are attached to the first and last kernel.
 hipError_t launch_plan(const int32_t *rowptr, int64_t M, Thresholds th,
                        const PlanBuffers &buf, float *C, int64_t N,
-                       hipStream_t stream);
+                       hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
 // Enqueue a kernel that writes chunk descriptors 0..count-1 (table entry or
 // recomputed) to out; used only by the plan export.
@@ -92,13 +97,15 @@ struct WorkerArgs {
     const void *B;
     float *C;
     int64_t M;
+    int64_t K;
     int64_t N;
     Thresholds th;
     PlanBuffers plan;
 };
 
+// start/stop (may be null) time the worker kernel.
 hipError_t launch_worker(const WorkerConfig &cfg, const WorkerArgs &args,
-                         hipStream_t stream);
+                         hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
 }  // namespace sdl
 

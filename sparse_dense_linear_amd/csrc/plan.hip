@@ -23,6 +23,8 @@
 //                chunk; the last tile writes the totals.  Optionally zeroes
 //                the C rows of long rows, which the worker accumulates into
 //                with atomics.
+#include <hip/hip_ext.h>
+
 #include "internal.h"
 
 namespace sdl {
@@ -32,7 +34,7 @@ PlanShape plan_shape(int64_t M)
     // At least 1024 rows per tile and at most kPlanMaxTiles tiles, so the
     // sum over earlier tiles in plan_scatter stays a few loads per thread.
     int64_t per = (M + kPlanMaxTiles - 1) / kPlanMaxTiles;
-    per = (per + kPlanBlock - 1) / kPlanBlock * kPlanBlock;
+    per = (per + 1023) / 1024 * 1024;
     PlanShape s;
     s.tile_rows = per < 1024 ? 1024 : per;
     s.n_tiles = (M + s.tile_rows - 1) / s.tile_rows;
@@ -52,7 +54,9 @@ __device__ inline RowClass classify(int64_t len, const Thresholds &th)
     RowClass c;
     c.medium = (len > th.short_max) && (len <= th.medium_max);
     c.lng = len > th.medium_max;
-    c.chunks = c.lng ? (int)((len + th.chunk_nnz - 1) / th.chunk_nnz) : 0;
+    // len < 2^31 and chunk_nnz < 2^31, so the 32-bit unsigned sum is exact
+    c.chunks = c.lng ? (int)(((uint32_t)len + (uint32_t)th.chunk_nnz - 1u) /
+                             (uint32_t)th.chunk_nnz) : 0;
     return c;
 }
 
@@ -100,6 +104,35 @@ __device__ inline int block_exclusive_scan(int v, int *total, int *red)
     return before + x - v;
 }
 
+// Rows handled per thread per round: a round covers kPlanBlock * 4 rows.
+constexpr int kRowsPerThread = 4;
+constexpr int64_t kRoundRows = (int64_t)kPlanBlock * kRowsPerThread;
+
+// Extents of the kRowsPerThread consecutive rows a thread owns in a round
+// (rows past r1 get length 0 and are flagged invalid).
+struct RowQuad {
+    int64_t start[kRowsPerThread];
+    int64_t len[kRowsPerThread];
+    bool valid[kRowsPerThread];
+};
+
+__device__ inline RowQuad load_quad(const int32_t *__restrict__ rowptr,
+                                    int64_t rb, int64_t r1)
+{
+    RowQuad q;
+    int64_t rp[kRowsPerThread + 1];
+#pragma unroll
+    for (int k = 0; k <= kRowsPerThread; ++k)
+        rp[k] = rb + k <= r1 ? rowptr[rb + k] : 0;
+#pragma unroll
+    for (int k = 0; k < kRowsPerThread; ++k) {
+        q.valid[k] = rb + k < r1;
+        q.start[k] = rp[k];
+        q.len[k] = q.valid[k] ? rp[k + 1] - rp[k] : 0;
+    }
+    return q;
+}
+
 __global__ __launch_bounds__(kPlanBlock) void plan_count_kernel(
     const int32_t *__restrict__ rowptr, int64_t M, int64_t tile_rows,
     Thresholds th, int32_t *__restrict__ tile_counts)
@@ -108,13 +141,18 @@ __global__ __launch_bounds__(kPlanBlock) void plan_count_kernel(
     const int64_t r0 = (int64_t)blockIdx.x * tile_rows;
     const int64_t r1 = r0 + tile_rows < M ? r0 + tile_rows : M;
     int med = 0, lng = 0, chunks = 0, shrt = 0;
-    for (int64_t r = r0 + threadIdx.x; r < r1; r += kPlanBlock) {
-        const int64_t len = (int64_t)rowptr[r + 1] - rowptr[r];
-        const RowClass c = classify(len, th);
-        med += c.medium;
-        lng += c.lng;
-        chunks += c.chunks;
-        shrt += !(c.medium | c.lng);
+    for (int64_t base = r0; base < r1; base += kRoundRows) {
+        const RowQuad q = load_quad(rowptr, base + kRowsPerThread * threadIdx.x, r1);
+#pragma unroll
+        for (int k = 0; k < kRowsPerThread; ++k) {
+            if (!q.valid[k])
+                continue;
+            const RowClass c = classify(q.len[k], th);
+            med += c.medium;
+            lng += c.lng;
+            chunks += c.chunks;
+            shrt += !(c.medium | c.lng);
+        }
     }
     med = block_sum(med, red);
     lng = block_sum(lng, red);
@@ -135,9 +173,20 @@ __global__ __launch_bounds__(kPlanBlock) void plan_scatter_kernel(
     int64_t N, int zero_long)
 {
     __shared__ int red[kPlanBlock / kWave];
-    __shared__ int long_list[kPlanBlock];
+    // This round's long rows: row, first chunk (relative to the round),
+    // chunk count, first position and length.
+    __shared__ int ll_row[kRoundRows];
+    __shared__ int ll_cfirst[kRoundRows];
+    __shared__ int ll_n[kRoundRows];
+    __shared__ int ll_start[kRoundRows];
+    __shared__ int ll_len[kRoundRows];
     const int64_t b = blockIdx.x;
     const int32_t *tc = pb.tile_counts;
+    const int64_t r0 = b * tile_rows;
+    const int64_t r1 = r0 + tile_rows < M ? r0 + tile_rows : M;
+
+    // Issue the first round's row loads before summing the earlier tiles.
+    RowQuad q = load_quad(rowptr, r0 + kRowsPerThread * threadIdx.x, r1);
 
     // Offsets of this tile = sums over all earlier tiles.
     int med_off = 0, long_off = 0, chunk_off = 0, short_off = 0;
@@ -160,57 +209,84 @@ __global__ __launch_bounds__(kPlanBlock) void plan_scatter_kernel(
         *pb.counts = total;
     }
 
-    const int64_t r0 = b * tile_rows;
-    const int64_t r1 = r0 + tile_rows < M ? r0 + tile_rows : M;
-    for (int64_t base = r0; base < r1; base += kPlanBlock) {
-        const int64_t r = base + threadIdx.x;
-        int64_t start = 0, len = 0;
-        if (r < r1) {
-            start = rowptr[r];
-            len = (int64_t)rowptr[r + 1] - start;
+    for (int64_t base = r0; base < r1; base += kRoundRows) {
+        const int64_t rb = base + kRowsPerThread * threadIdx.x;
+        if (base != r0)
+            q = load_quad(rowptr, rb, r1);
+        RowClass c[kRowsPerThread];
+        int my_flags = 0, my_chunks = 0;
+#pragma unroll
+        for (int k = 0; k < kRowsPerThread; ++k) {
+            c[k] = q.valid[k] ? classify(q.len[k], th) : RowClass{0, 0, 0};
+            my_flags += c[k].medium | (c[k].lng << 16);
+            my_chunks += c[k].chunks;
         }
-        const RowClass c = r < r1 ? classify(len, th) : RowClass{0, 0, 0};
-        // medium and long flags share one scan: counts per round fit 16 bits
+        // medium and long counts share one scan (a round has < 2^16 rows)
         int flags_total, chunk_total;
-        const int flags = block_exclusive_scan(c.medium | (c.lng << 16),
-                                               &flags_total, red);
-        const int cpos = block_exclusive_scan(c.chunks, &chunk_total, red);
-        if (c.medium)
-            pb.medium_rows[med_off + (flags & 0xFFFF)] = (int32_t)r;
-        if (c.lng) {
-            const int li = long_off + (flags >> 16);
-            const int first = chunk_off + cpos;
-            LongRow lr;
-            lr.row = (int32_t)r;
-            lr.first_chunk = first;
-            lr.n_chunks = c.chunks;
-            pb.long_rows[li] = lr;
-            for (int k = 0; k < c.chunks; ++k) {
-                const int64_t ci = (int64_t)first + k;
+        const int flags = block_exclusive_scan(my_flags, &flags_total, red);
+        int cpos = block_exclusive_scan(my_chunks, &chunk_total, red);
+        int mpos = med_off + (flags & 0xFFFF);
+        int lpos = flags >> 16;
+#pragma unroll
+        for (int k = 0; k < kRowsPerThread; ++k) {
+            const int64_t r = rb + k;
+            if (c[k].medium)
+                pb.medium_rows[mpos++] = (int32_t)r;
+            if (c[k].lng) {
+                LongRow lr;
+                lr.row = (int32_t)r;
+                lr.first_chunk = chunk_off + cpos;
+                lr.n_chunks = c[k].chunks;
+                pb.long_rows[long_off + lpos] = lr;
+                ll_row[lpos] = (int)r;
+                ll_cfirst[lpos] = cpos;
+                ll_n[lpos] = c[k].chunks;
+                ll_start[lpos] = (int)q.start[k];
+                ll_len[lpos] = (int)q.len[k];
+                ++lpos;
+                cpos += c[k].chunks;
+            }
+        }
+        const int n_long_here = flags_total >> 16;
+        if (n_long_here > 0) {
+            __syncthreads();
+            // Chunk descriptors of this round, all threads together: chunk x
+            // belongs to the last long row whose first chunk is <= x.
+            for (int x = threadIdx.x; x < chunk_total; x += kPlanBlock) {
+                const int64_t ci = (int64_t)chunk_off + x;
                 if (ci >= pb.chunk_cap)
                     break;
+                int lo = 0, hi = n_long_here - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (ll_cfirst[mid] <= x)
+                        lo = mid;
+                    else
+                        hi = mid - 1;
+                }
                 Chunk ch;
-                ch.row = (int32_t)r;
-                ch.long_idx = li;
-                chunk_bounds(start, len, c.chunks, k, &ch.p0, &ch.p1);
+                ch.row = ll_row[lo];
+                ch.long_idx = long_off + lo;
+                chunk_bounds(ll_start[lo], ll_len[lo], ll_n[lo], x - ll_cfirst[lo],
+                             &ch.p0, &ch.p1);
                 pb.chunks[ci] = ch;
             }
-            long_list[flags >> 16] = (int)(r - base);
-        }
-        med_off += flags_total & 0xFFFF;
-        long_off += flags_total >> 16;
-        chunk_off += chunk_total;
-        // Clear the C rows of this round's long rows, all threads together.
-        const int n_long_here = flags_total >> 16;
-        if (zero_long && n_long_here > 0) {
-            __syncthreads();
-            for (int q = 0; q < n_long_here; ++q) {
-                float *crow = C + (base + long_list[q]) * N;
-                for (int64_t n = threadIdx.x; n < N; n += kPlanBlock)
-                    crow[n] = 0.0f;
+            // Clear the C rows of this round's long rows.
+            if (zero_long) {
+                // one row per wavefront at a time, lanes across the columns
+                const int lane = threadIdx.x & (kWave - 1);
+                for (int x = threadIdx.x / kWave; x < n_long_here;
+                     x += kPlanBlock / kWave) {
+                    float *crow = C + (int64_t)ll_row[x] * N;
+                    for (int64_t n = lane; n < N; n += kWave)
+                        crow[n] = 0.0f;
+                }
             }
             __syncthreads();
         }
+        med_off += flags_total & 0xFFFF;
+        long_off += n_long_here;
+        chunk_off += chunk_total;
     }
 }
 
@@ -218,20 +294,21 @@ __global__ __launch_bounds__(kPlanBlock) void plan_scatter_kernel(
 
 hipError_t launch_plan(const int32_t *rowptr, int64_t M, Thresholds th,
                        const PlanBuffers &buf, float *C, int64_t N,
-                       hipStream_t stream)
+                       hipStream_t stream, hipEvent_t start, hipEvent_t stop)
 {
     const PlanShape s = plan_shape(M);
     if (s.n_tiles == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(plan_count_kernel, dim3((unsigned)s.n_tiles),
-                       dim3(kPlanBlock), 0, stream, rowptr, M, s.tile_rows,
-                       th, buf.tile_counts);
+    hipExtLaunchKernelGGL(plan_count_kernel, dim3((unsigned)s.n_tiles),
+                          dim3(kPlanBlock), 0, stream, start, nullptr, 0,
+                          rowptr, M, s.tile_rows, th, buf.tile_counts);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    hipLaunchKernelGGL(plan_scatter_kernel, dim3((unsigned)s.n_tiles),
-                       dim3(kPlanBlock), 0, stream, rowptr, M, s.tile_rows,
-                       s.n_tiles, th, buf, C, N, C != nullptr ? 1 : 0);
+    hipExtLaunchKernelGGL(plan_scatter_kernel, dim3((unsigned)s.n_tiles),
+                          dim3(kPlanBlock), 0, stream, nullptr, stop, 0,
+                          rowptr, M, s.tile_rows, s.n_tiles, th, buf, C, N,
+                          C != nullptr ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -32,12 +32,19 @@
 //                   with fp32 atomics (the row was zeroed by the plan);
 //       medium row  from the plan: as a chunk over the whole row, but the
 //                   result is stored, not added;
-//       short tile  a block of consecutive rows in natural order: each group
-//                   takes one row per pass (one row per group: RB with
-//                   coarsened columns); rows that are not short are skipped,
-//                   they belong to the other two kinds.
+//       short tile  a block of T consecutive rows in natural order.  The
+//                   entries of its short rows are staged in LDS in one round
+//                   (column, value and the row they belong to); each group
+//                   then streams the entries of its own P consecutive rows in
+//                   batches of U gathers that run across row boundaries,
+//                   storing a row of C when its last entry is consumed (one
+//                   row per group at a time: RB with coarsened columns).
+//                   Rows that are not short are skipped: they belong to the
+//                   other two kinds.
 //   * Within an item, U gathers per lane are issued back to back before any
 //     of them is consumed.
+#include <hip/hip_ext.h>
+
 #include "internal.h"
 #include "spmm.h"
 
@@ -53,28 +60,39 @@ __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // Loads of VEC consecutive elements of B and their exact widening to fp32.
+// load() takes a flat address; load_buf() a byte offset into a buffer
+// resource covering B (used when B is below 4 GiB: one 32-bit offset per
+// gather instead of a 64-bit address).
 template <int DT, int VEC> struct BLoad;
 
 template <> struct BLoad<SPMM_DTYPE_F32, 4> {
     typedef f32x4 raw;
     static __device__ raw load(const void *p) { return *(const f32x4 *)p; }
+    static __device__ raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off)
+    { return __builtin_bit_cast(raw, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0)); }
     static __device__ void widen(const raw &r, float (&o)[4])
     { o[0] = r.x; o[1] = r.y; o[2] = r.z; o[3] = r.w; }
 };
 template <> struct BLoad<SPMM_DTYPE_F32, 2> {
     typedef f32x2 raw;
     static __device__ raw load(const void *p) { return *(const f32x2 *)p; }
+    static __device__ raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off)
+    { return __builtin_bit_cast(raw, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0)); }
     static __device__ void widen(const raw &r, float (&o)[2])
     { o[0] = r.x; o[1] = r.y; }
 };
 template <> struct BLoad<SPMM_DTYPE_F32, 1> {
     typedef float raw;
     static __device__ raw load(const void *p) { return *(const float *)p; }
+    static __device__ raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off)
+    { return __builtin_bit_cast(raw, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0)); }
     static __device__ void widen(const raw &r, float (&o)[1]) { o[0] = r; }
 };
 template <> struct BLoad<SPMM_DTYPE_BF16, 8> {
     typedef u32x4 raw;
     static __device__ raw load(const void *p) { return *(const u32x4 *)p; }
+    static __device__ raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off)
+    { return __builtin_bit_cast(raw, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0)); }
     static __device__ void widen(const raw &r, float (&o)[8])
     {
         o[0] = bf16_lo(r.x); o[1] = bf16_hi(r.x);
@@ -86,6 +104,8 @@ template <> struct BLoad<SPMM_DTYPE_BF16, 8> {
 template <> struct BLoad<SPMM_DTYPE_BF16, 4> {
     typedef u32x2 raw;
     static __device__ raw load(const void *p) { return *(const u32x2 *)p; }
+    static __device__ raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off)
+    { return __builtin_bit_cast(raw, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0)); }
     static __device__ void widen(const raw &r, float (&o)[4])
     {
         o[0] = bf16_lo(r.x); o[1] = bf16_hi(r.x);
@@ -95,12 +115,16 @@ template <> struct BLoad<SPMM_DTYPE_BF16, 4> {
 template <> struct BLoad<SPMM_DTYPE_BF16, 2> {
     typedef uint32_t raw;
     static __device__ raw load(const void *p) { return *(const uint32_t *)p; }
+    static __device__ raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off)
+    { return __builtin_bit_cast(raw, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0)); }
     static __device__ void widen(const raw &r, float (&o)[2])
     { o[0] = bf16_lo(r); o[1] = bf16_hi(r); }
 };
 template <> struct BLoad<SPMM_DTYPE_BF16, 1> {
     typedef uint16_t raw;
     static __device__ raw load(const void *p) { return *(const uint16_t *)p; }
+    static __device__ raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off)
+    { return __builtin_bit_cast(raw, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0)); }
     static __device__ void widen(const raw &r, float (&o)[1])
     { o[0] = __uint_as_float((uint32_t)r << 16); }
 };
@@ -109,11 +133,38 @@ template <int DT> struct ElemSize;
 template <> struct ElemSize<SPMM_DTYPE_F32> { static constexpr int v = 4; };
 template <> struct ElemSize<SPMM_DTYPE_BF16> { static constexpr int v = 2; };
 
+// Word 3 of a raw buffer resource on the gfx9 family (gfx950): 32-bit
+// elements, no swizzle; with stride 0 the record count is a byte count and
+// loads past it return zero.
+constexpr int kBufferWord3 = 0x00020000;
+
 // A stored entry as staged in LDS: column and value (already fp32).
 struct Entry {
     int32_t col;
     float val;
 };
+
+// Per-wavefront LDS staging area.  A short tile stages at most kShortCap
+// entries (the host sizes tiles so that T * short_max <= kShortCap); medium
+// rows and long chunks use the first 64 entries.
+struct WaveStage {
+    Entry ent[kShortCap];
+    uint8_t rid[kShortCap];   // row of the entry within its tile
+};
+
+// Exclusive prefix sum of v over the 64 lanes of the wavefront.
+__device__ inline int wave_exclusive_sum(int v)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off)
+            x += y;
+    }
+    return x - v;
+}
 
 template <int DT> __device__ inline float load_val(const void *vals, int64_t p);
 template <> __device__ inline float load_val<SPMM_DTYPE_F32>(const void *vals, int64_t p)
@@ -122,8 +173,9 @@ template <> __device__ inline float load_val<SPMM_DTYPE_BF16>(const void *vals, 
 { return __uint_as_float((uint32_t)((const uint16_t *)vals)[p] << 16); }
 
 // Compile-time shape of one worker variant.
-template <int DT_, int VEC_, int G_, int NV_>
+template <int DT_, int VEC_, int G_, int NV_, bool BUF_>
 struct Shape {
+    static constexpr bool BUF = BUF_;   // B addressed through a buffer resource
     static constexpr int DT = DT_;
     static constexpr int VEC = VEC_;
     static constexpr int G = G_;
@@ -131,49 +183,105 @@ struct Shape {
     static constexpr int R = kWave / G_;          // groups per wavefront
     static constexpr int COLS = G_ * VEC_ * NV_;  // columns per column pass
     static constexpr int U = NV_ == 1 ? 8 : (NV_ == 2 ? 4 : 2);  // gathers in flight
+    static constexpr int ESZ = ElemSize<DT_>::v;
 };
+
+// Byte offsets (within a row of B) of this lane's NV vectors for the column
+// pass starting at col0, and whether each lies inside the row.  Lanes past
+// the end of the row read the row's last full vector instead, so every load
+// has a valid address and none needs a branch.
+template <class S>
+struct LaneCols {
+    int64_t ofs[S::NV];
+    bool live[S::NV];
+};
+
+template <class S>
+__device__ inline LaneCols<S> lane_cols(int64_t N, int64_t col0, int j)
+{
+    LaneCols<S> lc;
+#pragma unroll
+    for (int k = 0; k < S::NV; ++k) {
+        const int64_t c = col0 + (int64_t)(k * S::G + j) * S::VEC;
+        lc.live[k] = c < N;
+        lc.ofs[k] = (c < N ? c : N - S::VEC) * S::ESZ;
+    }
+    return lc;
+}
+
+// Where B lives: a buffer resource (BUF) or a flat pointer.
+struct BSrc {
+    __amdgpu_buffer_rsrc_t rsrc;
+    const char *base;
+};
+
+// One batch of up to U gathers of a lane group: the raw B vectors and the
+// entry values.
+template <class S>
+struct Batch {
+    typename BLoad<S::DT, S::VEC>::raw buf[S::U][S::NV];
+    float v[S::U];
+};
+
+// Issue the gathers of entries st[q .. q+n) (1 <= n <= U) back to back, with
+// no branches: slots past n repeat entry q.  The caller masks those slots
+// when accumulating.
+template <class S>
+__device__ inline void issue(Batch<S> &bt, const Entry *st, int q, int n,
+                             const BSrc &src, uint32_t row_bytes,
+                             const LaneCols<S> &lc)
+{
+    typedef BLoad<S::DT, S::VEC> L;
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+        const Entry e = st[u < n ? q + u : q];
+        bt.v[u] = e.val;
+        if constexpr (S::BUF) {
+            const uint32_t row = (uint32_t)e.col * row_bytes;
+#pragma unroll
+            for (int k = 0; k < S::NV; ++k)
+                bt.buf[u][k] = L::load_buf(src.rsrc, row + (uint32_t)lc.ofs[k]);
+        } else {
+            const char *row = src.base + (uint64_t)(uint32_t)e.col * row_bytes;
+#pragma unroll
+            for (int k = 0; k < S::NV; ++k)
+                bt.buf[u][k] = L::load(row + lc.ofs[k]);
+        }
+    }
+}
+
+// acc += v[u] * B-vector[u] when `on`; otherwise acc is left as it was (a
+// select, not a branch, so the value of an unused slot never matters).
+template <class S>
+__device__ inline void accumulate(const Batch<S> &bt, int u, bool on,
+                                  float (&acc)[S::NV][S::VEC])
+{
+    typedef BLoad<S::DT, S::VEC> L;
+#pragma unroll
+    for (int k = 0; k < S::NV; ++k) {
+        float b[S::VEC];
+        L::widen(bt.buf[u][k], b);
+#pragma unroll
+        for (int x = 0; x < S::VEC; ++x) {
+            const float t = fmaf(bt.v[u], b[x], acc[k][x]);
+            acc[k][x] = on ? t : acc[k][x];
+        }
+    }
+}
 
 // Group-local SAXPY over cnt staged entries: acc += val * B[col, cols of lane].
 template <class S>
-__device__ inline void consume(const Entry *st, int cnt, const void *B,
-                               int64_t N, int64_t col0, int j,
+__device__ inline void consume(const Entry *st, int cnt, const BSrc &src,
+                               uint32_t row_bytes, const LaneCols<S> &lc,
                                float (&acc)[S::NV][S::VEC])
 {
-    typedef BLoad<S::DT, S::VEC> L;
-    const char *Bb = (const char *)B;
     for (int u = 0; u < cnt; u += S::U) {
-        typename L::raw buf[S::U][S::NV];
-        float v[S::U];
+        const int n = cnt - u < S::U ? cnt - u : S::U;
+        Batch<S> bt;
+        issue<S>(bt, st, u, n, src, row_bytes, lc);
 #pragma unroll
-        for (int q = 0; q < S::U; ++q) {
-            if (u + q < cnt) {
-                const Entry e = st[u + q];
-                v[q] = e.val;
-                const int64_t rowoff = (int64_t)e.col * N + col0;
-#pragma unroll
-                for (int k = 0; k < S::NV; ++k) {
-                    const int64_t c = (int64_t)(k * S::G + j) * S::VEC;
-                    if (col0 + c < N)
-                        buf[q][k] = L::load(Bb + (rowoff + c) * ElemSize<S::DT>::v);
-                }
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < S::U; ++q) {
-            if (u + q < cnt) {
-#pragma unroll
-                for (int k = 0; k < S::NV; ++k) {
-                    const int64_t c = (int64_t)(k * S::G + j) * S::VEC;
-                    if (col0 + c < N) {
-                        float b[S::VEC];
-                        L::widen(buf[q][k], b);
-#pragma unroll
-                        for (int x = 0; x < S::VEC; ++x)
-                            acc[k][x] = fmaf(v[q], b[x], acc[k][x]);
-                    }
-                }
-            }
-        }
+        for (int x = 0; x < S::U; ++x)
+            accumulate<S>(bt, x, x < n, acc);
     }
 }
 
@@ -231,22 +339,21 @@ __device__ inline void reduce_groups(float (&acc)[S::NV][S::VEC])
                 acc[k][x] += __shfl_xor(acc[k][x], off);
 }
 
-// One wavefront accumulates positions [p0, p1) of one row: 64-entry chunks
-// of colind/vals are loaded coalesced (the next one prefetched into
+// One wavefront accumulates positions [p0, p1) (p1 > p0) of one row: 64-entry
+// chunks of colind/vals are loaded coalesced (the next one prefetched into
 // registers while the current one is consumed) and staged in LDS; group g
 // consumes entries g*G .. g*G+G-1 of each chunk.
 template <class S>
 __device__ inline void wave_range(const WorkerArgs &a, Entry *st, int lane,
-                                  int g, int j, int64_t p0, int64_t p1,
-                                  int64_t col0, float (&acc)[S::NV][S::VEC])
+                                  int g, int64_t p0, int64_t p1,
+                                  const BSrc &src, const LaneCols<S> &lc,
+                                  uint32_t row_bytes, float (&acc)[S::NV][S::VEC])
 {
     zero_acc<S>(acc);
-    int32_t nc = 0;
-    float nvv = 0.0f;
-    if (p0 + lane < p1) {
-        nc = a.colind[p0 + lane];
-        nvv = load_val<S::DT>(a.vals, p0 + lane);
-    }
+    // positions past the range read the range's last entry (valid address)
+    int64_t p = p0 + lane < p1 ? p0 + lane : p1 - 1;
+    int32_t nc = a.colind[p];
+    float nvv = load_val<S::DT>(a.vals, p);
     for (int64_t base = p0; base < p1; base += kWave) {
         const int n = p1 - base < kWave ? (int)(p1 - base) : kWave;
         if (lane < n) {
@@ -256,24 +363,27 @@ __device__ inline void wave_range(const WorkerArgs &a, Entry *st, int lane,
             st[lane] = e;
         }
         const int64_t nb = base + kWave;
-        if (nb + lane < p1) {
-            nc = a.colind[nb + lane];
-            nvv = load_val<S::DT>(a.vals, nb + lane);
+        if (nb < p1) {
+            p = nb + lane < p1 ? nb + lane : p1 - 1;
+            nc = a.colind[p];
+            nvv = load_val<S::DT>(a.vals, p);
         }
         int cnt = n - g * S::G;
         cnt = cnt < 0 ? 0 : (cnt > S::G ? S::G : cnt);
-        consume<S>(st + g * S::G, cnt, a.B, a.N, col0, j, acc);
+        consume<S>(st + g * S::G, cnt, src, row_bytes, lc, acc);
     }
 }
 
 template <class S>
 __device__ void do_chunk(const WorkerArgs &a, Entry *st, int lane, int g,
-                         int j, int64_t c, int32_t n_long)
+                         int j, int64_t c, int32_t n_long, const BSrc &src,
+                         uint32_t row_bytes)
 {
     const Chunk ch = resolve_chunk(c, a.plan, n_long, a.rowptr);
     for (int64_t col0 = 0; col0 < a.N; col0 += S::COLS) {
+        const LaneCols<S> lc = lane_cols<S>(a.N, col0, j);
         float acc[S::NV][S::VEC];
-        wave_range<S>(a, st, lane, g, j, ch.p0, ch.p1, col0, acc);
+        wave_range<S>(a, st, lane, g, ch.p0, ch.p1, src, lc, row_bytes, acc);
         reduce_groups<S>(acc);
         if (g == 0)
             emit_row<S, true>(a.C, ch.row, a.N, col0, j, acc);
@@ -282,56 +392,98 @@ __device__ void do_chunk(const WorkerArgs &a, Entry *st, int lane, int g,
 
 template <class S>
 __device__ void do_medium(const WorkerArgs &a, Entry *st, int lane, int g,
-                          int j, int64_t i)
+                          int j, int64_t i, const BSrc &src, uint32_t row_bytes)
 {
     const int64_t row = a.plan.medium_rows[i];
     const int64_t p0 = a.rowptr[row];
     const int64_t p1 = a.rowptr[row + 1];
     for (int64_t col0 = 0; col0 < a.N; col0 += S::COLS) {
+        const LaneCols<S> lc = lane_cols<S>(a.N, col0, j);
         float acc[S::NV][S::VEC];
-        wave_range<S>(a, st, lane, g, j, p0, p1, col0, acc);
+        wave_range<S>(a, st, lane, g, p0, p1, src, lc, row_bytes, acc);
         reduce_groups<S>(acc);
         if (g == 0)
             emit_row<S, false>(a.C, row, a.N, col0, j, acc);
     }
 }
 
-// A short tile is `passes` passes of R consecutive rows (passes * R <= 64).
+// One short tile: rows r0 .. r0+T-1 with T = P*R; group g owns rows
+// g*P .. g*P+P-1 of the tile.
 template <class S>
-__device__ void do_short_tile(const WorkerArgs &a, Entry *st, int lane, int g,
-                              int j, int64_t t, int passes)
+__device__ void do_short_tile(const WorkerArgs &a, WaveStage &ws, int lane,
+                              int g, int j, int64_t t, int P,
+                              const BSrc &src, uint32_t row_bytes)
 {
-    const int tile = passes * S::R;
-    const int64_t r0 = t * tile;
-    // lane l < tile holds the extent of row r0 + l
-    int32_t s = 0, e = 0;
-    if (lane < tile && r0 + lane < a.M) {
-        s = a.rowptr[r0 + lane];
-        e = a.rowptr[r0 + lane + 1];
+    const int T = P * S::R;
+    const int64_t r0 = t * (int64_t)T;
+    const int64_t r = r0 + lane;
+    const bool in_tile = lane < T && r < a.M;
+    int32_t s = 0, len = 0;
+    if (in_tile) {
+        s = a.rowptr[r];
+        len = a.rowptr[r + 1] - s;
     }
-    Entry *sg = st + g * S::G;
-#pragma unroll 1
-    for (int pass = 0; pass < passes; ++pass) {
-        const int src = pass * S::R + g;
-        const int32_t start = __shfl(s, src);
-        const int32_t end = __shfl(e, src);
-        const int64_t row = r0 + src;
-        if (row >= a.M || end - start > a.th.short_max)
-            continue;  // past the end, or routed to the medium/long kinds
-        for (int64_t col0 = 0; col0 < a.N; col0 += S::COLS) {
-            float acc[S::NV][S::VEC];
-            zero_acc<S>(acc);
-            for (int32_t base = start; base < end; base += S::G) {
-                const int cnt = end - base < S::G ? end - base : S::G;
-                if (j < cnt) {
-                    Entry en;
-                    en.col = a.colind[base + j];
-                    en.val = load_val<S::DT>(a.vals, base + j);
-                    sg[j] = en;
-                }
-                consume<S>(sg, cnt, a.B, a.N, col0, j, acc);
+    const bool shrt = in_tile && len <= a.th.short_max;
+    const int slen = shrt ? len : 0;
+    const int off = wave_exclusive_sum(slen);
+
+    // Stage the tile's short entries, flattened in row order: entry e goes
+    // to lane e % 64.  The lane finds the row holding e (the last lane l with
+    // off_l <= e; such a lane has slen_l > 0) by a binary search over the
+    // lanes' offsets, so each round is one coalesced load per lane however
+    // the entries are spread over rows.
+    const int total = __shfl(off + slen, kWave - 1);
+    for (int e0 = 0; e0 < total; e0 += kWave) {
+        const int e = e0 + lane < total ? e0 + lane : total - 1;
+        int l = 0;
+#pragma unroll
+        for (int step = kWave / 2; step > 0; step >>= 1) {
+            const int cand = l + step;
+            if (__shfl(off, cand) <= e)
+                l = cand;
+        }
+        const int64_t p = (int64_t)__shfl(s, l) + (e - __shfl(off, l));
+        Entry en;
+        en.col = a.colind[p];
+        en.val = load_val<S::DT>(a.vals, p);
+        if (e0 + lane < total) {
+            ws.ent[e] = en;
+            ws.rid[e] = (uint8_t)l;
+        }
+    }
+
+    const int first = g * P;
+    const int beg = __shfl(off, first);
+    const int end = __shfl(off + slen, first + P - 1);
+    const int empty = (shrt && len == 0) ? 1 : 0;
+
+    for (int64_t col0 = 0; col0 < a.N; col0 += S::COLS) {
+        const LaneCols<S> lc = lane_cols<S>(a.N, col0, j);
+        // Empty short rows are rows of zeros.
+        for (int q = 0; q < P; ++q) {
+            if (__shfl(empty, first + q)) {
+                float z[S::NV][S::VEC];
+                zero_acc<S>(z);
+                emit_row<S, false>(a.C, r0 + first + q, a.N, col0, j, z);
             }
-            emit_row<S, false>(a.C, row, a.N, col0, j, acc);
+        }
+        float acc[S::NV][S::VEC];
+        zero_acc<S>(acc);
+        for (int q = beg; q < end; q += S::U) {
+            const int n = end - q < S::U ? end - q : S::U;
+            Batch<S> bt;
+            issue<S>(bt, ws.ent, q, n, src, row_bytes, lc);
+#pragma unroll
+            for (int u = 0; u < S::U; ++u) {
+                accumulate<S>(bt, u, u < n, acc);
+                if (u < n) {
+                    const int rr = ws.rid[q + u];
+                    if (q + u + 1 == end || ws.rid[q + u + 1] != rr) {
+                        emit_row<S, false>(a.C, r0 + rr, a.N, col0, j, acc);
+                        zero_acc<S>(acc);
+                    }
+                }
+            }
         }
     }
 }
@@ -352,12 +504,13 @@ __global__ __launch_bounds__(kBlock) void worker_kernel(WorkerArgs a,
                                                         int passes,
                                                         int64_t total_waves)
 {
-    __shared__ Entry stage[kWavesPerBlock][kWave];
+    __shared__ WaveStage stage[kWavesPerBlock];
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = threadIdx.x / kWave;
     const int g = lane / S::G;
     const int j = lane % S::G;
-    Entry *st = stage[wid];
+    WaveStage &ws = stage[wid];
+    Entry *st = ws.ent;
 
     const PlanCounts pc = *a.plan.counts;
     const int64_t n_ch = pc.n_chunks;
@@ -365,18 +518,27 @@ __global__ __launch_bounds__(kBlock) void worker_kernel(WorkerArgs a,
     const int64_t n_items = n_ch + n_med + n_tiles;
     const int64_t w0 = xcd_logical_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wid;
 
+    const uint32_t row_bytes = (uint32_t)(a.N * S::ESZ);
+    BSrc src;
+    src.base = (const char *)a.B;
+    if constexpr (S::BUF)
+        src.rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<void *>(a.B), (short)0,
+            (int)(uint32_t)(a.K * a.N * S::ESZ), kBufferWord3);
     for (int64_t item = w0; item < n_items; item += total_waves) {
         if (item < n_ch)
-            do_chunk<S>(a, st, lane, g, j, item, pc.n_long);
+            do_chunk<S>(a, st, lane, g, j, item, pc.n_long, src, row_bytes);
         else if (item < n_ch + n_med)
-            do_medium<S>(a, st, lane, g, j, item - n_ch);
+            do_medium<S>(a, st, lane, g, j, item - n_ch, src, row_bytes);
         else
-            do_short_tile<S>(a, st, lane, g, j, item - n_ch - n_med, passes);
+            do_short_tile<S>(a, ws, lane, g, j, item - n_ch - n_med, passes,
+                             src, row_bytes);
     }
 }
 
 template <class S>
-hipError_t launch_shape(const WorkerArgs &a, hipStream_t stream)
+hipError_t launch_shape(const WorkerArgs &a, hipStream_t stream,
+                        hipEvent_t start, hipEvent_t stop)
 {
     static int resident_blocks = 0;  // per variant: blocks that fit at once
     if (resident_blocks == 0) {
@@ -391,41 +553,45 @@ hipError_t launch_shape(const WorkerArgs &a, hipStream_t stream)
             return err;
         resident_blocks = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
     }
-    // Short tiles: up to 8 passes of R rows (at most 64 rows), fewer when M
-    // is too small to give every resident wavefront a tile.
+    // Short tiles: P rows per group (T = P*R rows, at most 64), at most 8,
+    // small enough that the staged entries fit (T * short_max <= kShortCap),
+    // and fewer when M is too small to give every resident wavefront a tile.
     const int64_t resident_waves = (int64_t)resident_blocks * kWavesPerBlock;
+    const int64_t smax = a.th.short_max > 1 ? a.th.short_max : 1;
+    int64_t max_passes = kWave / S::R < 8 ? kWave / S::R : 8;
+    if (max_passes > kShortCap / (S::R * smax))
+        max_passes = kShortCap / (S::R * smax);
+    if (max_passes < 1)
+        return hipErrorInvalidValue;  // short_max above the group capacity
     int64_t passes = a.M / ((int64_t)S::R * resident_waves);
-    const int64_t max_passes = kWave / S::R < 8 ? kWave / S::R : 8;
     passes = passes < 1 ? 1 : (passes > max_passes ? max_passes : passes);
     const int64_t tile = passes * S::R;
     const int64_t n_tiles = (a.M + tile - 1) / tile;
-    // Items: chunks (unknown on the host) + medium rows (<= M) + tiles.
-    const int64_t want_waves = n_tiles + a.M;
-    int64_t blocks = (want_waves + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (blocks > resident_blocks)
-        blocks = resident_blocks;
-    if (blocks < 1)
-        blocks = 1;
-    hipLaunchKernelGGL(worker_kernel<S>, dim3((unsigned)blocks), dim3(kBlock),
-                       0, stream, a, n_tiles, (int)passes,
-                       blocks * kWavesPerBlock);
+    // The number of long-row chunks is known only on the device, so the
+    // grid is every block that fits at once; waves without work exit after
+    // reading the plan counts.
+    const int64_t blocks = resident_blocks;
+    hipExtLaunchKernelGGL(worker_kernel<S>, dim3((unsigned)blocks), dim3(kBlock),
+                          0, stream, start, stop, 0, a, n_tiles, (int)passes,
+                          blocks * kWavesPerBlock);
     return hipGetLastError();
 }
 
-template <int DT, int VEC>
-hipError_t launch_vec(int group, int nv, const WorkerArgs &a, hipStream_t s)
+template <int DT, int VEC, bool BUF>
+hipError_t launch_vec(int group, int nv, const WorkerArgs &a, hipStream_t s,
+                      hipEvent_t e0, hipEvent_t e1)
 {
     switch (group) {
-    case 1: return launch_shape<Shape<DT, VEC, 1, 1>>(a, s);
-    case 2: return launch_shape<Shape<DT, VEC, 2, 1>>(a, s);
-    case 4: return launch_shape<Shape<DT, VEC, 4, 1>>(a, s);
-    case 8: return launch_shape<Shape<DT, VEC, 8, 1>>(a, s);
-    case 16: return launch_shape<Shape<DT, VEC, 16, 1>>(a, s);
-    case 32: return launch_shape<Shape<DT, VEC, 32, 1>>(a, s);
+    case 1: return launch_shape<Shape<DT, VEC, 1, 1, BUF>>(a, s, e0, e1);
+    case 2: return launch_shape<Shape<DT, VEC, 2, 1, BUF>>(a, s, e0, e1);
+    case 4: return launch_shape<Shape<DT, VEC, 4, 1, BUF>>(a, s, e0, e1);
+    case 8: return launch_shape<Shape<DT, VEC, 8, 1, BUF>>(a, s, e0, e1);
+    case 16: return launch_shape<Shape<DT, VEC, 16, 1, BUF>>(a, s, e0, e1);
+    case 32: return launch_shape<Shape<DT, VEC, 32, 1, BUF>>(a, s, e0, e1);
     case 64:
-        if (nv == 1) return launch_shape<Shape<DT, VEC, 64, 1>>(a, s);
-        if (nv == 2) return launch_shape<Shape<DT, VEC, 64, 2>>(a, s);
-        return launch_shape<Shape<DT, VEC, 64, 4>>(a, s);
+        if (nv == 1) return launch_shape<Shape<DT, VEC, 64, 1, BUF>>(a, s, e0, e1);
+        if (nv == 2) return launch_shape<Shape<DT, VEC, 64, 2, BUF>>(a, s, e0, e1);
+        return launch_shape<Shape<DT, VEC, 64, 4, BUF>>(a, s, e0, e1);
     default: return hipErrorInvalidValue;
     }
 }
@@ -459,24 +625,37 @@ WorkerConfig choose_worker(int dtype, int64_t N, const void *B, const float *C)
     return cfg;
 }
 
-hipError_t launch_worker(const WorkerConfig &cfg, const WorkerArgs &a,
-                         hipStream_t s)
+template <bool BUF>
+hipError_t launch_dtype(const WorkerConfig &cfg, const WorkerArgs &a,
+                        hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
     if (cfg.dtype == SPMM_DTYPE_F32) {
         switch (cfg.vec) {
-        case 4: return launch_vec<SPMM_DTYPE_F32, 4>(cfg.group, cfg.nv, a, s);
-        case 2: return launch_vec<SPMM_DTYPE_F32, 2>(cfg.group, cfg.nv, a, s);
-        case 1: return launch_vec<SPMM_DTYPE_F32, 1>(cfg.group, cfg.nv, a, s);
+        case 4: return launch_vec<SPMM_DTYPE_F32, 4, BUF>(cfg.group, cfg.nv, a, s, e0, e1);
+        case 2: return launch_vec<SPMM_DTYPE_F32, 2, BUF>(cfg.group, cfg.nv, a, s, e0, e1);
+        case 1: return launch_vec<SPMM_DTYPE_F32, 1, BUF>(cfg.group, cfg.nv, a, s, e0, e1);
         }
     } else {
         switch (cfg.vec) {
-        case 8: return launch_vec<SPMM_DTYPE_BF16, 8>(cfg.group, cfg.nv, a, s);
-        case 4: return launch_vec<SPMM_DTYPE_BF16, 4>(cfg.group, cfg.nv, a, s);
-        case 2: return launch_vec<SPMM_DTYPE_BF16, 2>(cfg.group, cfg.nv, a, s);
-        case 1: return launch_vec<SPMM_DTYPE_BF16, 1>(cfg.group, cfg.nv, a, s);
+        case 8: return launch_vec<SPMM_DTYPE_BF16, 8, BUF>(cfg.group, cfg.nv, a, s, e0, e1);
+        case 4: return launch_vec<SPMM_DTYPE_BF16, 4, BUF>(cfg.group, cfg.nv, a, s, e0, e1);
+        case 2: return launch_vec<SPMM_DTYPE_BF16, 2, BUF>(cfg.group, cfg.nv, a, s, e0, e1);
+        case 1: return launch_vec<SPMM_DTYPE_BF16, 1, BUF>(cfg.group, cfg.nv, a, s, e0, e1);
         }
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_worker(const WorkerConfig &cfg, const WorkerArgs &a,
+                         hipStream_t s, hipEvent_t e0, hipEvent_t e1)
+{
+    // B is addressed through a buffer resource (32-bit byte offsets) when it
+    // is below 4 GiB, otherwise through flat 64-bit addresses.
+    const int esz = cfg.dtype == SPMM_DTYPE_BF16 ? 2 : 4;
+    const uint64_t b_bytes = (uint64_t)a.K * (uint64_t)a.N * (uint64_t)esz;
+    if (b_bytes < 0xFFFFFFFFull)
+        return launch_dtype<true>(cfg, a, s, e0, e1);
+    return launch_dtype<false>(cfg, a, s, e0, e1);
 }
 
 }  // namespace sdl
