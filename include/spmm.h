@@ -155,11 +155,13 @@ const char *spmm_last_error(void);
 
 /*
  * Kernel timing for benchmarks.  spmm_timing_enable(1) makes every later
- * call record HIP events around its planning kernels and around its
- * worker kernel on the call's stream; spmm_timing_read waits for the
- * recorded events, returns the summed milliseconds and the number of calls
- * timed, and clears the record.  Disabled by default; enabling adds two
- * event records per call.
+ * call attach HIP events to the dispatches of its two kernels (the plan,
+ * then the product), so timing adds no packets to the stream.
+ * spmm_timing_read waits for the recorded events and returns the summed
+ * milliseconds of the timed calls: *plan_ms from the start of the plan
+ * kernel to the start of the product kernel (the plan and the gap between
+ * the two), *worker_ms the product kernel's own duration; *calls is their
+ * number.  It then clears the record.  Disabled by default.
  */
 spmm_status_t spmm_timing_enable(int32_t on);
 spmm_status_t spmm_timing_read(double *plan_ms, double *worker_ms,

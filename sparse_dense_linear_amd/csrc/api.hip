@@ -1,9 +1,9 @@
 // api.hip -- host side of the C ABI declared in include/spmm.h.
 //
 // Checks arguments before any HIP call, resolves the routing thresholds,
-// takes one call's scratch space (the row plan) from a stream-ordered pool,
-// enqueues the planning kernels and the worker kernel, and returns without
-// waiting for the device.
+// takes the stream's scratch space (the row plan), enqueues the one kernel
+// that plans and computes the product, and returns without waiting for the
+// device.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -124,28 +124,34 @@ hipError_t pool_for_device(int dev, hipMemPool_t *out)
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
-// Byte offsets of the plan arrays inside one scratch block.
+// Byte offsets of the plan arrays inside one scratch block (see
+// PlanBuffers).  The block is zeroed when created; words are tagged with a
+// per-call epoch, so a block can serve calls of any M up to its size.
 struct ScratchLayout {
-    int64_t tile_counts, counts, medium_rows, long_rows, chunks, total;
+    int64_t counts, agg, medium_rows, long_row,
+        long_first, chunk_row, chunk_k, total;
     int64_t chunk_cap;
 };
 
 ScratchLayout scratch_layout(int64_t M)
 {
-    const PlanShape s = plan_shape(M);
     ScratchLayout l;
     int64_t off = 0;
-    l.tile_counts = off;
-    off = align_up(off + 16 * s.n_tiles, 256);
     l.counts = off;
-    off = align_up(off + (int64_t)sizeof(PlanCounts), 256);
+    off = align_up(off + 4 * 8, 256);
+    l.agg = off;
+    off = align_up(off + 8 * 3 * kPlanMaxTiles, 256);
     l.medium_rows = off;
-    off = align_up(off + 4 * M, 256);
-    l.long_rows = off;
-    off = align_up(off + (int64_t)sizeof(LongRow) * M, 256);
+    off = align_up(off + 8 * M, 256);
+    l.long_row = off;
+    off = align_up(off + 8 * M, 256);
+    l.long_first = off;
+    off = align_up(off + 8 * M, 256);
     l.chunk_cap = M + kChunkTableSlack;
-    l.chunks = off;
-    off = align_up(off + (int64_t)sizeof(Chunk) * l.chunk_cap, 256);
+    l.chunk_row = off;
+    off = align_up(off + 8 * l.chunk_cap, 256);
+    l.chunk_k = off;
+    off = align_up(off + 8 * l.chunk_cap, 256);
     l.total = off;
     return l;
 }
@@ -153,11 +159,13 @@ ScratchLayout scratch_layout(int64_t M)
 PlanBuffers carve(char *base, const ScratchLayout &l)
 {
     PlanBuffers b;
-    b.tile_counts = (int32_t *)(base + l.tile_counts);
-    b.counts = (PlanCounts *)(base + l.counts);
-    b.medium_rows = (int32_t *)(base + l.medium_rows);
-    b.long_rows = (LongRow *)(base + l.long_rows);
-    b.chunks = (Chunk *)(base + l.chunks);
+    b.counts = (uint64_t *)(base + l.counts);
+    b.agg = (uint64_t *)(base + l.agg);
+    b.medium_rows = (uint64_t *)(base + l.medium_rows);
+    b.long_row = (uint64_t *)(base + l.long_row);
+    b.long_first = (uint64_t *)(base + l.long_first);
+    b.chunk_row = (uint64_t *)(base + l.chunk_row);
+    b.chunk_k = (uint64_t *)(base + l.chunk_k);
     b.chunk_cap = l.chunk_cap;
     return b;
 }
@@ -169,51 +177,75 @@ bool test_fail_alloc()
 }
 
 // Scratch space is kept per (device, stream) and reused by later calls on
-// the same stream, which stream order serialises; it grows (allocate the
-// larger block, free the old one, both stream-ordered) when a call needs
-// more.  Calls on different streams never share scratch.
+// the same stream, which stream order serialises.  A block that is too
+// small is replaced (allocate and zero the larger one, free the old one,
+// all stream-ordered).  Calls on different streams never share scratch.
+// Each call on a block gets the next epoch; epoch 0 never occurs, so the
+// zeroed block holds no valid word.
 struct StreamScratch {
     int dev;
     hipStream_t stream;
     void *ptr;
     size_t size;
+    uint32_t epoch;   // last epoch used on this block
 };
 
 std::mutex g_scratch_mu;
 std::vector<StreamScratch> g_scratch;
 
-hipError_t scratch_for(int dev, hipStream_t stream, size_t need, void **out)
+hipError_t fresh_block(int dev, hipStream_t stream, size_t size, void **out)
 {
-    std::lock_guard<std::mutex> lock(g_scratch_mu);
-    StreamScratch *slot = nullptr;
-    for (StreamScratch &e : g_scratch)
-        if (e.dev == dev && e.stream == stream)
-            slot = &e;
-    if (slot && slot->size >= need) {
-        *out = slot->ptr;
-        return hipSuccess;
-    }
     hipMemPool_t pool;
     hipError_t err = pool_for_device(dev, &pool);
     if (err != hipSuccess)
         return err;
-    size_t size = need;
-    if (slot && size < slot->size + slot->size / 4)
-        size = slot->size + slot->size / 4;
     void *ptr = nullptr;
     err = hipMallocFromPoolAsync(&ptr, size, pool, stream);
     if (err != hipSuccess)
         return err;
     if (ptr == nullptr)
         return hipErrorOutOfMemory;
+    err = hipMemsetAsync(ptr, 0, size, stream);
+    if (err != hipSuccess) {
+        hipFreeAsync(ptr, stream);
+        return err;
+    }
+    *out = ptr;
+    return hipSuccess;
+}
+
+// Scratch block of at least `need` bytes for this stream, and the epoch the
+// caller's launch must use.
+hipError_t scratch_for(int dev, hipStream_t stream, size_t need, void **out,
+                       uint32_t *epoch)
+{
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    StreamScratch *slot = nullptr;
+    for (StreamScratch &e : g_scratch)
+        if (e.dev == dev && e.stream == stream)
+            slot = &e;
+    if (slot && slot->size >= need && slot->epoch != UINT32_MAX) {
+        *out = slot->ptr;
+        *epoch = ++slot->epoch;
+        return hipSuccess;
+    }
+    size_t size = need;
+    if (slot && size < slot->size + slot->size / 4)
+        size = slot->size + slot->size / 4;
+    void *ptr = nullptr;
+    hipError_t err = fresh_block(dev, stream, size, &ptr);
+    if (err != hipSuccess)
+        return err;
     if (slot) {
         hipFreeAsync(slot->ptr, stream);
         slot->ptr = ptr;
         slot->size = size;
+        slot->epoch = 1;
     } else {
-        g_scratch.push_back(StreamScratch{dev, stream, ptr, size});
+        g_scratch.push_back(StreamScratch{dev, stream, ptr, size, 1});
     }
     *out = ptr;
+    *epoch = 1;
     return hipSuccess;
 }
 
@@ -223,7 +255,9 @@ hipError_t scratch_for(int dev, hipStream_t stream, size_t need, void **out)
 // packets themselves (hipExtLaunchKernel), so timing adds no packets to the
 // stream.  Events are recycled through a free list.
 struct TimedCall {
-    hipEvent_t plan0, plan1, work0, work1;
+    hipEvent_t plan0;  // start of the plan kernel
+    hipEvent_t work0;  // start of the product kernel
+    hipEvent_t work1;  // end of the product kernel
 };
 
 std::mutex g_time_mu;
@@ -296,17 +330,12 @@ spmm_status_t run(int32_t dtype, const int32_t *rowptr, const int32_t *colind,
         return fail_hip(err, "hipGetDevice");
     const ScratchLayout lay = scratch_layout(M);
     void *scratch = nullptr;
-    err = scratch_for(dev, stream, (size_t)lay.total, &scratch);
+    uint32_t epoch = 0;
+    err = scratch_for(dev, stream, (size_t)lay.total, &scratch, &epoch);
     if (err == hipErrorOutOfMemory)
         return fail(SPMM_ERROR_OUT_OF_MEMORY, "scratch allocation failed");
     if (err != hipSuccess)
         return fail_hip(err, "scratch allocation");
-
-    const PlanBuffers pb = carve((char *)scratch, lay);
-    Thresholds th;
-    th.short_max = t.short_max;
-    th.medium_max = t.medium_max;
-    th.chunk_nnz = t.chunk_nnz;
 
     TimedCall tc{};
     bool timing;
@@ -315,15 +344,10 @@ spmm_status_t run(int32_t dtype, const int32_t *rowptr, const int32_t *colind,
         timing = g_timing;
         if (timing &&
             ((err = take_event(&tc.plan0)) != hipSuccess ||
-             (err = take_event(&tc.plan1)) != hipSuccess ||
              (err = take_event(&tc.work0)) != hipSuccess ||
              (err = take_event(&tc.work1)) != hipSuccess))
             return fail_hip(err, "hipEventCreate");
     }
-
-    err = launch_plan(rowptr, M, th, pb, C, N, stream, tc.plan0, tc.plan1);
-    if (err != hipSuccess)
-        return fail_hip(err, "plan kernels");
 
     WorkerArgs wa;
     wa.rowptr = rowptr;
@@ -334,10 +358,14 @@ spmm_status_t run(int32_t dtype, const int32_t *rowptr, const int32_t *colind,
     wa.M = M;
     wa.K = K;
     wa.N = N;
-    wa.th = th;
-    wa.plan = pb;
+    wa.th.short_max = t.short_max;
+    wa.th.medium_max = t.medium_max;
+    wa.th.chunk_nnz = t.chunk_nnz;
+    wa.plan = carve((char *)scratch, lay);
+    wa.shape = plan_shape(M);
+    wa.epoch = epoch;
     const WorkerConfig cfg = choose_worker(dtype, N, B, C);
-    err = launch_worker(cfg, wa, stream, tc.work0, tc.work1);
+    err = launch_worker(cfg, wa, stream, tc.plan0, tc.work0, tc.work1);
     if (err != hipSuccess)
         return fail_hip(err, "worker kernel");
     if (timing) {
@@ -413,57 +441,67 @@ spmm_status_t spmm_plan_export(const int32_t *rowptr, int64_t M,
 
     hipStream_t stream = (hipStream_t)stream_ptr;
     const ScratchLayout lay = scratch_layout(M);
-    void *scratch = nullptr;
-    hipError_t err = hipMalloc(&scratch, (size_t)lay.total);
+    const int64_t recs = cap > 0 ? cap : 1;
+    char *dev_mem = nullptr;
+    // scratch, then the exported arrays and counts
+    const int64_t off_med = align_up(lay.total, 256);
+    const int64_t off_long = align_up(off_med + 4 * recs, 256);
+    const int64_t off_chunk = align_up(off_long + (int64_t)sizeof(LongRow) * recs, 256);
+    const int64_t off_counts = align_up(off_chunk + (int64_t)sizeof(Chunk) * recs, 256);
+    const int64_t total = off_counts + 4 * 8;
+    hipError_t err = hipMalloc(&dev_mem, (size_t)total);
     if (err != hipSuccess)
         return fail_hip(err, "hipMalloc");
-    const PlanBuffers pb = carve((char *)scratch, lay);
-    Thresholds th;
-    th.short_max = resolved->short_max;
-    th.medium_max = resolved->medium_max;
-    th.chunk_nnz = resolved->chunk_nnz;
-    Chunk *expanded = nullptr;
     spmm_status_t st = SPMM_SUCCESS;
-    PlanCounts pc;
     do {
-        if ((err = launch_plan(rowptr, M, th, pb, nullptr, 0, stream, nullptr, nullptr)) != hipSuccess ||
-            (err = hipMemcpyAsync(&pc, pb.counts, sizeof pc, hipMemcpyDeviceToHost,
-                                  stream)) != hipSuccess ||
-            (err = hipStreamSynchronize(stream)) != hipSuccess) {
+        if ((err = hipMemsetAsync(dev_mem, 0, (size_t)lay.total, stream)) != hipSuccess) {
+            st = fail_hip(err, "hipMemsetAsync");
+            break;
+        }
+        WorkerArgs wa;
+        memset(&wa, 0, sizeof wa);
+        wa.rowptr = rowptr;
+        wa.M = M;
+        wa.N = 1;
+        wa.th.short_max = resolved->short_max;
+        wa.th.medium_max = resolved->medium_max;
+        wa.th.chunk_nnz = resolved->chunk_nnz;
+        wa.plan = carve(dev_mem, lay);
+        wa.shape = plan_shape(M);
+        wa.epoch = 1;
+        wa.C = nullptr;  // plan only
+        const WorkerConfig cfg = choose_worker(SPMM_DTYPE_F32, 1, nullptr, nullptr);
+        int64_t dcounts[4];
+        if ((err = launch_worker(cfg, wa, stream, nullptr, nullptr, nullptr)) != hipSuccess ||
+            (err = launch_plan_export(rowptr, M, wa.th, wa.plan, 1, cap,
+                                      (int32_t *)(dev_mem + off_med),
+                                      (LongRow *)(dev_mem + off_long),
+                                      (Chunk *)(dev_mem + off_chunk),
+                                      (int64_t *)(dev_mem + off_counts), stream)) != hipSuccess ||
+            (err = hipStreamSynchronize(stream)) != hipSuccess ||
+            (err = hipMemcpy(dcounts, dev_mem + off_counts, sizeof dcounts,
+                             hipMemcpyDeviceToHost)) != hipSuccess) {
             st = fail_hip(err, "plan");
             break;
         }
-        counts[0] = pc.n_short;
-        counts[1] = pc.n_medium;
-        counts[2] = pc.n_long;
-        counts[3] = pc.n_chunks;
-        const int64_t nm = pc.n_medium < cap ? pc.n_medium : cap;
-        const int64_t nl = pc.n_long < cap ? pc.n_long : cap;
-        const int64_t nc = pc.n_chunks < cap ? pc.n_chunks : cap;
-        if (nm > 0 && (err = hipMemcpy(medium_rows, pb.medium_rows, 4 * nm,
-                                       hipMemcpyDeviceToHost)) != hipSuccess) {
-            st = fail_hip(err, "copy medium rows");
+        for (int q = 0; q < 4; ++q)
+            counts[q] = dcounts[q];
+        const int64_t nm = dcounts[1] < cap ? dcounts[1] : cap;
+        const int64_t nl = dcounts[2] < cap ? dcounts[2] : cap;
+        const int64_t nc = dcounts[3] < cap ? dcounts[3] : cap;
+        if ((nm > 0 && (err = hipMemcpy(medium_rows, dev_mem + off_med, 4 * nm,
+                                        hipMemcpyDeviceToHost)) != hipSuccess) ||
+            (nl > 0 && (err = hipMemcpy(long_rows, dev_mem + off_long,
+                                        sizeof(LongRow) * nl,
+                                        hipMemcpyDeviceToHost)) != hipSuccess) ||
+            (nc > 0 && (err = hipMemcpy(chunks, dev_mem + off_chunk,
+                                        sizeof(Chunk) * nc,
+                                        hipMemcpyDeviceToHost)) != hipSuccess)) {
+            st = fail_hip(err, "copy plan");
             break;
-        }
-        if (nl > 0 && (err = hipMemcpy(long_rows, pb.long_rows, sizeof(LongRow) * nl,
-                                       hipMemcpyDeviceToHost)) != hipSuccess) {
-            st = fail_hip(err, "copy long rows");
-            break;
-        }
-        if (nc > 0) {
-            if ((err = hipMalloc(&expanded, sizeof(Chunk) * nc)) != hipSuccess ||
-                (err = launch_chunk_expand(rowptr, th, pb, nc, expanded, stream)) != hipSuccess ||
-                (err = hipStreamSynchronize(stream)) != hipSuccess ||
-                (err = hipMemcpy(chunks, expanded, sizeof(Chunk) * nc,
-                                 hipMemcpyDeviceToHost)) != hipSuccess) {
-                st = fail_hip(err, "expand chunks");
-                break;
-            }
         }
     } while (0);
-    if (expanded)
-        hipFree(expanded);
-    hipFree(scratch);
+    hipFree(dev_mem);
     return st;
 }
 
@@ -503,7 +541,7 @@ spmm_status_t spmm_timing_read(double *plan_ms, double *worker_ms,
         float a = 0.0f, b = 0.0f;
         hipError_t err = hipEventSynchronize(tc.work1);
         if (err == hipSuccess)
-            err = hipEventElapsedTime(&a, tc.plan0, tc.plan1);
+            err = hipEventElapsedTime(&a, tc.plan0, tc.work0);
         if (err == hipSuccess)
             err = hipEventElapsedTime(&b, tc.work0, tc.work1);
         if (err != hipSuccess && st == SPMM_SUCCESS)
@@ -515,7 +553,6 @@ spmm_status_t spmm_timing_read(double *plan_ms, double *worker_ms,
         std::lock_guard<std::mutex> lock(g_time_mu);
         for (const TimedCall &tc : taken) {
             g_free_events.push_back(tc.plan0);
-            g_free_events.push_back(tc.plan1);
             g_free_events.push_back(tc.work0);
             g_free_events.push_back(tc.work1);
         }

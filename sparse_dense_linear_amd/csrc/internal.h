@@ -10,8 +10,9 @@ namespace sdl {
 constexpr int kWave = 64;            // CDNA wavefront width
 constexpr int kWavesPerBlock = 4;    // worker block = 256 threads
 constexpr int kBlock = kWave * kWavesPerBlock;
-constexpr int kPlanBlock = 256;      // planning kernels: threads per block
-constexpr int kPlanMaxTiles = 2048;  // planning tiles per call (upper bound)
+constexpr int kPlanLaneRows = 4;     // plan rows per lane per round
+constexpr int kPlanRoundRows = kWave * kPlanLaneRows;  // rows per plan round
+constexpr int kPlanMaxTiles = 1024;  // plan tiles per call (upper bound)
 constexpr int64_t kChunkTableSlack = 4096;  // chunk table holds M + this
 // Entries of one short tile staged per wavefront; short_max is capped at
 // kShortCap / R (R = row groups per wavefront) so that a tile of at least R
@@ -25,41 +26,8 @@ struct Thresholds {
     int32_t chunk_nnz;
 };
 
-// Per long row: the row, the index of its first chunk, its chunk count.
-struct LongRow {
-    int32_t row;
-    int32_t first_chunk;
-    int32_t n_chunks;
-};
-
-// One nnz chunk of a long row: positions [p0, p1) of row `row`, which is
-// entry `long_idx` of the long-row list.
-struct Chunk {
-    int32_t row;
-    int32_t p0;
-    int32_t p1;
-    int32_t long_idx;
-};
-
-// Totals the planning pass leaves on the device for the worker.
-struct PlanCounts {
-    int32_t n_medium;
-    int32_t n_long;
-    int32_t n_chunks;
-    int32_t n_short;
-};
-
-// Device pointers into one call's scratch space.
-struct PlanBuffers {
-    int32_t *tile_counts;   // [n_tiles * 4]: medium, long, chunks, short
-    PlanCounts *counts;     // [1]
-    int32_t *medium_rows;   // [M]
-    LongRow *long_rows;     // [M]
-    Chunk *chunks;          // [chunk_cap]
-    int64_t chunk_cap;
-};
-
-// Shape of the planning pass over M rows: n_tiles blocks of tile_rows rows.
+// Shape of the plan over M rows: n_tiles wavefront tiles of tile_rows rows
+// (a multiple of kPlanRoundRows).
 struct PlanShape {
     int64_t tile_rows;
     int64_t n_tiles;
@@ -67,24 +35,41 @@ struct PlanShape {
 
 PlanShape plan_shape(int64_t M);
 
-// Enqueue the two planning kernels.  When zero_long_rows is set, the C rows
-// of long rows (leading dimension N) are cleared for atomic accumulation.
-// start/stop (may be null) are attached to the first and last kernel.
-hipError_t launch_plan(const int32_t *rowptr, int64_t M, Thresholds th,
-                       const PlanBuffers &buf, float *C, int64_t N,
-                       hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+// The plan lives in scratch memory that is kept per stream and reused by
+// every call on it.  Each word the plan publishes is tagged with the call's
+// epoch (upper 32 bits; the value in the lower 32), written and read with
+// device-coherent relaxed atomics; a reader waits until the tag equals the
+// current epoch.  Epochs start at 1 and grow by one per call, and the
+// scratch is zeroed when it is created, so no word needs clearing between
+// calls.
+struct PlanBuffers {
+    uint64_t *counts;        // [4] n_medium, n_long, n_chunks, n_short
+    uint64_t *agg;           // [3 * kPlanMaxTiles] per tile: medium, long, chunks
+    uint64_t *medium_rows;   // [M] rows with short_max < len <= medium_max
+    uint64_t *long_row;      // [M] long rows, ascending
+    uint64_t *long_first;    // [M] index of each long row's first chunk
+    uint64_t *chunk_row;     // [chunk_cap] row of each chunk
+    uint64_t *chunk_k;       // [chunk_cap] position of the chunk in its row
+    int64_t chunk_cap;       // M + kChunkTableSlack
+};
 
-// Enqueue a kernel that writes chunk descriptors 0..count-1 (table entry or
-// recomputed) to out; used only by the plan export.
-hipError_t launch_chunk_expand(const int32_t *rowptr, Thresholds th,
-                               const PlanBuffers &buf, int64_t count,
-                               Chunk *out, hipStream_t stream);
+// Bounds of chunk k of a long row that starts at `start`, holds `len`
+// entries and is cut into n chunks: positions
+// [start + floor(k*len/n), start + floor((k+1)*len/n)).  The chunks tile the
+// row in order and differ in size by at most one entry.
+__host__ __device__ inline void chunk_bounds(int64_t start, int64_t len,
+                                             int64_t n, int64_t k,
+                                             int64_t *p0, int64_t *p1)
+{
+    *p0 = start + (k * len) / n;
+    *p1 = start + ((k + 1) * len) / n;
+}
 
 // Worker configuration picked by the host for one call.
 struct WorkerConfig {
     int dtype;     // SPMM_DTYPE_*
     int vec;       // elements of B per lane load
-    int group;     // lanes per row group (G); R = 64 / G groups per wave
+    int group;     // lanes per row group (G); R = 64 / G groups per wavefront
     int nv;        // vectors per lane per B row (columns per pass = G*vec*nv)
 };
 
@@ -95,58 +80,46 @@ struct WorkerArgs {
     const int32_t *colind;
     const void *vals;
     const void *B;
-    float *C;
+    float *C;              // null: plan only (no product)
     int64_t M;
     int64_t K;
     int64_t N;
     Thresholds th;
     PlanBuffers plan;
+    PlanShape shape;
+    uint32_t epoch;
 };
 
-// start/stop (may be null) time the worker kernel.
+// Enqueue the plan kernel and then the product kernel (the plan alone when
+// a.C is null).  The events (each may be null) are attached to the
+// dispatches: plan_start to the start of the plan kernel, work_start and
+// work_stop to the start and the end of the product kernel.
 hipError_t launch_worker(const WorkerConfig &cfg, const WorkerArgs &args,
-                         hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+                         hipStream_t stream, hipEvent_t plan_start,
+                         hipEvent_t work_start, hipEvent_t work_stop);
 
-}  // namespace sdl
+// Plain descriptors for the plan export.
+struct LongRow {
+    int32_t row;
+    int32_t first_chunk;
+    int32_t n_chunks;
+};
 
-namespace sdl {
+struct Chunk {
+    int32_t row;
+    int32_t p0;
+    int32_t p1;
+    int32_t long_idx;
+};
 
-// Bounds of chunk k of a long row that starts at `start`, holds `len`
-// entries and is cut into n chunks: positions
-// [start + floor(k*len/n), start + floor((k+1)*len/n)).  The chunks tile the
-// row in order and differ in size by at most one entry.
-__host__ __device__ inline void chunk_bounds(int64_t start, int64_t len,
-                                             int64_t n, int64_t k,
-                                             int32_t *p0, int32_t *p1)
-{
-    *p0 = (int32_t)(start + (k * len) / n);
-    *p1 = (int32_t)(start + ((k + 1) * len) / n);
-}
-
-// Descriptor of chunk c: the table entry when c is inside the table,
-// otherwise recomputed from the long-row list (binary search for the last
-// long row whose first chunk is <= c) and rowptr.
-__device__ inline Chunk resolve_chunk(int64_t c, const PlanBuffers &pb,
-                                      int32_t n_long, const int32_t *rowptr)
-{
-    if (c < pb.chunk_cap)
-        return pb.chunks[c];
-    int32_t lo = 0, hi = n_long - 1;
-    while (lo < hi) {
-        const int32_t mid = (lo + hi + 1) >> 1;
-        if (pb.long_rows[mid].first_chunk <= c)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    const LongRow lr = pb.long_rows[lo];
-    const int64_t start = rowptr[lr.row];
-    const int64_t len = (int64_t)rowptr[lr.row + 1] - start;
-    Chunk ch;
-    ch.row = lr.row;
-    ch.long_idx = lo;
-    chunk_bounds(start, len, lr.n_chunks, c - lr.first_chunk, &ch.p0, &ch.p1);
-    return ch;
-}
+// Copy the tagged plan of a finished plan-only launch into plain device
+// arrays (at most `cap` records each; a record whose word does not carry
+// `epoch` is written as -1).  counts_out[4] gets n_short, n_medium, n_long,
+// n_chunks.  Enqueued on `stream`.
+hipError_t launch_plan_export(const int32_t *rowptr, int64_t M, Thresholds th,
+                              const PlanBuffers &pb, uint32_t epoch,
+                              int64_t cap, int32_t *medium_out,
+                              LongRow *long_out, Chunk *chunk_out,
+                              int64_t *counts_out, hipStream_t stream);
 
 }  // namespace sdl

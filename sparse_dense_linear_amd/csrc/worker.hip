@@ -46,6 +46,7 @@
 #include <hip/hip_ext.h>
 
 #include "internal.h"
+#include "plan_device.h"
 #include "spmm.h"
 
 namespace sdl {
@@ -151,6 +152,7 @@ struct WaveStage {
     Entry ent[kShortCap];
     uint8_t rid[kShortCap];   // row of the entry within its tile
 };
+
 
 // Exclusive prefix sum of v over the 64 lanes of the wavefront.
 __device__ inline int wave_exclusive_sum(int v)
@@ -374,36 +376,70 @@ __device__ inline void wave_range(const WorkerArgs &a, Entry *st, int lane,
     }
 }
 
-template <class S>
-__device__ void do_chunk(const WorkerArgs &a, Entry *st, int lane, int g,
-                         int j, int64_t c, int32_t n_long, const BSrc &src,
-                         uint32_t row_bytes)
+// Row and position range of chunk ci if its plan entries are published:
+// from the chunk table, or past its end from the long-row list (binary
+// search for the last long row whose first chunk is <= ci).  Never waits.
+__device__ inline bool chunk_ready(const WorkerArgs &a, int64_t ci,
+                                   int64_t n_long, int64_t *row, int64_t *p0,
+                                   int64_t *p1)
 {
-    const Chunk ch = resolve_chunk(c, a.plan, n_long, a.rowptr);
-    for (int64_t col0 = 0; col0 < a.N; col0 += S::COLS) {
-        const LaneCols<S> lc = lane_cols<S>(a.N, col0, j);
-        float acc[S::NV][S::VEC];
-        wave_range<S>(a, st, lane, g, ch.p0, ch.p1, src, lc, row_bytes, acc);
-        reduce_groups<S>(acc);
-        if (g == 0)
-            emit_row<S, true>(a.C, ch.row, a.N, col0, j, acc);
+    uint64_t wr, wk;
+    if (ci < a.plan.chunk_cap) {
+        wr = __shfl(tag_load(a.plan.chunk_row + ci), 0);
+        wk = __shfl(tag_load(a.plan.chunk_k + ci), 0);
+        if (!tag_is(wr, a.epoch) || !tag_is(wk, a.epoch))
+            return false;
+    } else {
+        int64_t lo = 0, hi = n_long - 1;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) >> 1;
+            const uint64_t wf = __shfl(tag_load(a.plan.long_first + mid), 0);
+            if (!tag_is(wf, a.epoch))
+                return false;
+            if ((int64_t)(uint32_t)wf <= ci)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        wr = __shfl(tag_load(a.plan.long_row + lo), 0);
+        const uint64_t wf = __shfl(tag_load(a.plan.long_first + lo), 0);
+        if (!tag_is(wr, a.epoch) || !tag_is(wf, a.epoch))
+            return false;
+        wk = (uint64_t)(ci - (int64_t)(uint32_t)wf);
     }
+    const int64_t r = (uint32_t)wr;
+    const int64_t start = a.rowptr[r];
+    const int64_t len = (int64_t)a.rowptr[r + 1] - start;
+    const int64_t n = (len + a.th.chunk_nnz - 1) / a.th.chunk_nnz;
+    chunk_bounds(start, len, n, (int64_t)(uint32_t)wk, p0, p1);
+    *row = r;
+    return true;
 }
 
-template <class S>
-__device__ void do_medium(const WorkerArgs &a, Entry *st, int lane, int g,
-                          int j, int64_t i, const BSrc &src, uint32_t row_bytes)
+// Row of medium item i if published.  Never waits.
+__device__ inline bool medium_ready(const WorkerArgs &a, int64_t i, int64_t *row)
 {
-    const int64_t row = a.plan.medium_rows[i];
-    const int64_t p0 = a.rowptr[row];
-    const int64_t p1 = a.rowptr[row + 1];
+    const uint64_t w = __shfl(tag_load(a.plan.medium_rows + i), 0);
+    if (!tag_is(w, a.epoch))
+        return false;
+    *row = (uint32_t)w;
+    return true;
+}
+
+// One wavefront accumulates row `row` over positions [p0, p1) and stores
+// (medium row) or atomically adds (long-row chunk) the result.
+template <class S, bool ATOMIC>
+__device__ void do_range(const WorkerArgs &a, WaveStage &ws, int lane, int g,
+                         int j, int64_t row, int64_t p0, int64_t p1,
+                         const BSrc &src, uint32_t row_bytes)
+{
     for (int64_t col0 = 0; col0 < a.N; col0 += S::COLS) {
         const LaneCols<S> lc = lane_cols<S>(a.N, col0, j);
         float acc[S::NV][S::VEC];
-        wave_range<S>(a, st, lane, g, p0, p1, src, lc, row_bytes, acc);
+        wave_range<S>(a, ws.ent, lane, g, p0, p1, src, lc, row_bytes, acc);
         reduce_groups<S>(acc);
         if (g == 0)
-            emit_row<S, false>(a.C, row, a.N, col0, j, acc);
+            emit_row<S, ATOMIC>(a.C, row, a.N, col0, j, acc);
     }
 }
 
@@ -498,6 +534,25 @@ __device__ inline int64_t xcd_logical_block(int64_t b, int64_t nb)
     return x * per + (x < rem ? x : rem) + k;
 }
 
+// Plan totals if this call's have been published (no waiting).
+__device__ inline bool counts_ready(const WorkerArgs &a, int64_t *n_med,
+                                    int64_t *n_long, int64_t *n_ch)
+{
+    const uint64_t w0 = __shfl(tag_load(a.plan.counts + 0), 0);
+    const uint64_t w1 = __shfl(tag_load(a.plan.counts + 1), 0);
+    const uint64_t w2 = __shfl(tag_load(a.plan.counts + 2), 0);
+    if (!tag_is(w0, a.epoch) || !tag_is(w1, a.epoch) || !tag_is(w2, a.epoch))
+        return false;
+    *n_med = (uint32_t)w0;
+    *n_long = (uint32_t)w1;
+    *n_ch = (uint32_t)w2;
+    return true;
+}
+
+// The product, after the plan kernel: every wavefront takes items w, w+W,
+// w+2W, ... of the list [long-row chunks | medium rows | short tiles].  A
+// plan entry that does not carry this call's epoch (the plan gave up) is
+// skipped, never waited for.
 template <class S>
 __global__ __launch_bounds__(kBlock) void worker_kernel(WorkerArgs a,
                                                         int64_t n_tiles,
@@ -510,13 +565,7 @@ __global__ __launch_bounds__(kBlock) void worker_kernel(WorkerArgs a,
     const int g = lane / S::G;
     const int j = lane % S::G;
     WaveStage &ws = stage[wid];
-    Entry *st = ws.ent;
-
-    const PlanCounts pc = *a.plan.counts;
-    const int64_t n_ch = pc.n_chunks;
-    const int64_t n_med = pc.n_medium;
-    const int64_t n_items = n_ch + n_med + n_tiles;
-    const int64_t w0 = xcd_logical_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wid;
+    const int64_t w = xcd_logical_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wid;
 
     const uint32_t row_bytes = (uint32_t)(a.N * S::ESZ);
     BSrc src;
@@ -525,14 +574,24 @@ __global__ __launch_bounds__(kBlock) void worker_kernel(WorkerArgs a,
         src.rsrc = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<void *>(a.B), (short)0,
             (int)(uint32_t)(a.K * a.N * S::ESZ), kBufferWord3);
-    for (int64_t item = w0; item < n_items; item += total_waves) {
-        if (item < n_ch)
-            do_chunk<S>(a, st, lane, g, j, item, pc.n_long, src, row_bytes);
-        else if (item < n_ch + n_med)
-            do_medium<S>(a, st, lane, g, j, item - n_ch, src, row_bytes);
-        else
+
+    int64_t n_med = 0, n_long = 0, n_ch = 0;
+    if (!counts_ready(a, &n_med, &n_long, &n_ch))
+        n_med = n_long = n_ch = 0;
+    const int64_t n_items = n_ch + n_med + n_tiles;
+    for (int64_t item = w; item < n_items; item += total_waves) {
+        int64_t row, p0, p1;
+        if (item < n_ch) {
+            if (chunk_ready(a, item, n_long, &row, &p0, &p1))
+                do_range<S, true>(a, ws, lane, g, j, row, p0, p1, src, row_bytes);
+        } else if (item < n_ch + n_med) {
+            if (medium_ready(a, item - n_ch, &row))
+                do_range<S, false>(a, ws, lane, g, j, row, a.rowptr[row],
+                                   a.rowptr[row + 1], src, row_bytes);
+        } else {
             do_short_tile<S>(a, ws, lane, g, j, item - n_ch - n_med, passes,
                              src, row_bytes);
+        }
     }
 }
 
@@ -582,8 +641,6 @@ hipError_t launch_vec(int group, int nv, const WorkerArgs &a, hipStream_t s,
                       hipEvent_t e0, hipEvent_t e1)
 {
     switch (group) {
-    case 1: return launch_shape<Shape<DT, VEC, 1, 1, BUF>>(a, s, e0, e1);
-    case 2: return launch_shape<Shape<DT, VEC, 2, 1, BUF>>(a, s, e0, e1);
     case 4: return launch_shape<Shape<DT, VEC, 4, 1, BUF>>(a, s, e0, e1);
     case 8: return launch_shape<Shape<DT, VEC, 8, 1, BUF>>(a, s, e0, e1);
     case 16: return launch_shape<Shape<DT, VEC, 16, 1, BUF>>(a, s, e0, e1);
@@ -612,7 +669,7 @@ WorkerConfig choose_worker(int dtype, int64_t N, const void *B, const float *C)
             break;
     }
     const int64_t vecs = (N + vec - 1) / vec;  // lane vectors per B row
-    int group = 1;
+    int group = 4;  // at least 4 lanes per row group
     while (group < 64 && group < vecs)
         group *= 2;
     int64_t nv = (vecs + group - 1) / group;
@@ -646,8 +703,8 @@ hipError_t launch_dtype(const WorkerConfig &cfg, const WorkerArgs &a,
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_worker(const WorkerConfig &cfg, const WorkerArgs &a,
-                         hipStream_t s, hipEvent_t e0, hipEvent_t e1)
+hipError_t launch_product(const WorkerConfig &cfg, const WorkerArgs &a,
+                          hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
     // B is addressed through a buffer resource (32-bit byte offsets) when it
     // is below 4 GiB, otherwise through flat 64-bit addresses.
