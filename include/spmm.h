@@ -155,17 +155,27 @@ const char *spmm_last_error(void);
 
 /*
  * Kernel timing for benchmarks.  spmm_timing_enable(1) makes every later
- * call attach HIP events to the dispatches of its two kernels (the plan,
- * then the product), so timing adds no packets to the stream.
- * spmm_timing_read waits for the recorded events and returns the summed
- * milliseconds of the timed calls: *plan_ms from the start of the plan
- * kernel to the start of the product kernel (the plan and the gap between
- * the two), *worker_ms the product kernel's own duration; *calls is their
- * number.  It then clears the record.  Disabled by default.
+ * call attach HIP events to the start and the end of its launch (a call is
+ * one launch: the plan runs in its first workgroups), so timing adds no
+ * packets to the stream.  spmm_timing_read waits for the recorded events
+ * and returns, in *worker_ms, the summed milliseconds of the timed calls
+ * and, in *calls, their number, then clears the record; *plan_ms is always
+ * 0 (the plan is inside the launch).  Disabled by default.
  */
 spmm_status_t spmm_timing_enable(int32_t on);
 spmm_status_t spmm_timing_read(double *plan_ms, double *worker_ms,
                                int64_t *calls);
+
+/*
+ * Health check for tests.  Inside a call, product wavefronts poll for the
+ * plan entries they need while the plan workgroups of the same launch write
+ * them; each poll is bounded (about a second), and an item whose entry
+ * never became visible is left undone and counted.  spmm_stream_faults
+ * waits for `stream`, returns in *faults the number of such items since the
+ * stream's scratch was created or last queried, and resets it.  The count
+ * is 0 unless the plan workgroups were kept from running.
+ */
+spmm_status_t spmm_stream_faults(void *stream, int64_t *faults);
 
 #ifdef __cplusplus
 }

@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     spmm_csr_f32,
     spmm_csr_tuned,
     status_string,
+    stream_faults,
     timing_enable,
     timing_read,
 )

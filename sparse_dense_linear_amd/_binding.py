@@ -76,9 +76,10 @@ def lib() -> ctypes.CDLL:
     L.spmm_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_int64)]
+    L.spmm_stream_faults.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]
     for name in ("spmm_csr_f32", "spmm_csr_bf16in_f32acc", "spmm_csr_tuned",
                  "spmm_resolve_tuning", "spmm_plan_export", "spmm_timing_enable",
-                 "spmm_timing_read"):
+                 "spmm_timing_read", "spmm_stream_faults"):
         getattr(L, name).restype = I32
     _lib = L
     return L
@@ -238,10 +239,19 @@ def timing_enable(on: bool = True) -> None:
 
 
 def timing_read() -> tuple[float, float, int]:
-    """(plan ms, worker ms, calls) summed over calls since the last read."""
+    """(0.0, call ms, calls) summed over the calls since the last read."""
     p = ctypes.c_double()
     w = ctypes.c_double()
     n = ctypes.c_int64()
     _check(lib().spmm_timing_read(ctypes.byref(p), ctypes.byref(w), ctypes.byref(n)),
            "spmm_timing_read")
     return p.value, w.value, n.value
+
+
+def stream_faults(stream=None) -> int:
+    """Items left undone because a plan entry never became visible, on
+    `stream` (default: torch's current stream), since the last query."""
+    n = ctypes.c_int64()
+    _check(lib().spmm_stream_faults(_stream_handle(None, stream), ctypes.byref(n)),
+           "spmm_stream_faults")
+    return n.value

@@ -128,7 +128,7 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 // PlanBuffers).  The block is zeroed when created; words are tagged with a
 // per-call epoch, so a block can serve calls of any M up to its size.
 struct ScratchLayout {
-    int64_t counts, agg, medium_rows, long_row,
+    int64_t counts, faults, agg, medium_rows, long_row,
         long_first, chunk_row, chunk_k, total;
     int64_t chunk_cap;
 };
@@ -139,8 +139,10 @@ ScratchLayout scratch_layout(int64_t M)
     int64_t off = 0;
     l.counts = off;
     off = align_up(off + 4 * 8, 256);
+    l.faults = off;
+    off = align_up(off + 4, 256);
     l.agg = off;
-    off = align_up(off + 8 * 3 * kPlanMaxTiles, 256);
+    off = align_up(off + 8 * 3 * kPlanMaxBlocks, 256);
     l.medium_rows = off;
     off = align_up(off + 8 * M, 256);
     l.long_row = off;
@@ -166,6 +168,7 @@ PlanBuffers carve(char *base, const ScratchLayout &l)
     b.long_first = (uint64_t *)(base + l.long_first);
     b.chunk_row = (uint64_t *)(base + l.chunk_row);
     b.chunk_k = (uint64_t *)(base + l.chunk_k);
+    b.faults = (uint32_t *)(base + l.faults);
     b.chunk_cap = l.chunk_cap;
     return b;
 }
@@ -255,9 +258,8 @@ hipError_t scratch_for(int dev, hipStream_t stream, size_t need, void **out,
 // packets themselves (hipExtLaunchKernel), so timing adds no packets to the
 // stream.  Events are recycled through a free list.
 struct TimedCall {
-    hipEvent_t plan0;  // start of the plan kernel
-    hipEvent_t work0;  // start of the product kernel
-    hipEvent_t work1;  // end of the product kernel
+    hipEvent_t work0;  // start of the call's launch
+    hipEvent_t work1;  // end of the call's launch
 };
 
 std::mutex g_time_mu;
@@ -343,8 +345,7 @@ spmm_status_t run(int32_t dtype, const int32_t *rowptr, const int32_t *colind,
         std::lock_guard<std::mutex> lock(g_time_mu);
         timing = g_timing;
         if (timing &&
-            ((err = take_event(&tc.plan0)) != hipSuccess ||
-             (err = take_event(&tc.work0)) != hipSuccess ||
+            ((err = take_event(&tc.work0)) != hipSuccess ||
              (err = take_event(&tc.work1)) != hipSuccess))
             return fail_hip(err, "hipEventCreate");
     }
@@ -365,7 +366,7 @@ spmm_status_t run(int32_t dtype, const int32_t *rowptr, const int32_t *colind,
     wa.shape = plan_shape(M);
     wa.epoch = epoch;
     const WorkerConfig cfg = choose_worker(dtype, N, B, C);
-    err = launch_worker(cfg, wa, stream, tc.plan0, tc.work0, tc.work1);
+    err = launch_worker(cfg, wa, stream, tc.work0, tc.work1);
     if (err != hipSuccess)
         return fail_hip(err, "worker kernel");
     if (timing) {
@@ -472,7 +473,7 @@ spmm_status_t spmm_plan_export(const int32_t *rowptr, int64_t M,
         wa.C = nullptr;  // plan only
         const WorkerConfig cfg = choose_worker(SPMM_DTYPE_F32, 1, nullptr, nullptr);
         int64_t dcounts[4];
-        if ((err = launch_worker(cfg, wa, stream, nullptr, nullptr, nullptr)) != hipSuccess ||
+        if ((err = launch_worker(cfg, wa, stream, nullptr, nullptr)) != hipSuccess ||
             (err = launch_plan_export(rowptr, M, wa.th, wa.plan, 1, cap,
                                       (int32_t *)(dev_mem + off_med),
                                       (LongRow *)(dev_mem + off_long),
@@ -541,8 +542,6 @@ spmm_status_t spmm_timing_read(double *plan_ms, double *worker_ms,
         float a = 0.0f, b = 0.0f;
         hipError_t err = hipEventSynchronize(tc.work1);
         if (err == hipSuccess)
-            err = hipEventElapsedTime(&a, tc.plan0, tc.work0);
-        if (err == hipSuccess)
             err = hipEventElapsedTime(&b, tc.work0, tc.work1);
         if (err != hipSuccess && st == SPMM_SUCCESS)
             st = fail_hip(err, "hipEventElapsedTime");
@@ -552,7 +551,6 @@ spmm_status_t spmm_timing_read(double *plan_ms, double *worker_ms,
     {
         std::lock_guard<std::mutex> lock(g_time_mu);
         for (const TimedCall &tc : taken) {
-            g_free_events.push_back(tc.plan0);
             g_free_events.push_back(tc.work0);
             g_free_events.push_back(tc.work1);
         }
@@ -564,6 +562,41 @@ spmm_status_t spmm_timing_read(double *plan_ms, double *worker_ms,
     if (calls)
         *calls = (int64_t)taken.size();
     return st;
+}
+
+spmm_status_t spmm_stream_faults(void *stream_ptr, int64_t *faults)
+{
+    g_last_error.clear();
+    if (faults == nullptr)
+        return fail(SPMM_ERROR_INVALID_VALUE, "faults is null");
+    *faults = 0;
+    hipStream_t stream = (hipStream_t)stream_ptr;
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return fail_hip(err, "hipGetDevice");
+    void *block = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        for (StreamScratch &e : g_scratch)
+            if (e.dev == dev && e.stream == stream)
+                block = e.ptr;
+    }
+    if (block == nullptr)
+        return SPMM_SUCCESS;  // no call on this stream yet
+    uint32_t *word = (uint32_t *)((char *)block + scratch_layout(0).faults);
+    uint32_t v = 0;
+    if ((err = hipMemcpyAsync(&v, word, sizeof v, hipMemcpyDeviceToHost, stream)) != hipSuccess ||
+        (err = hipStreamSynchronize(stream)) != hipSuccess)
+        return fail_hip(err, "reading the fault count");
+    if (v != 0) {
+        const uint32_t zero = 0;
+        if ((err = hipMemcpyAsync(word, &zero, sizeof zero, hipMemcpyHostToDevice, stream)) != hipSuccess ||
+            (err = hipStreamSynchronize(stream)) != hipSuccess)
+            return fail_hip(err, "clearing the fault count");
+    }
+    *faults = v;
+    return SPMM_SUCCESS;
 }
 
 }  // extern "C"

@@ -13,6 +13,10 @@ constexpr int kBlock = kWave * kWavesPerBlock;
 constexpr int kPlanLaneRows = 4;     // plan rows per lane per round
 constexpr int kPlanRoundRows = kWave * kPlanLaneRows;  // rows per plan round
 constexpr int kPlanMaxTiles = 1024;  // plan tiles per call (upper bound)
+constexpr int kPlanBlockWaves = kWavesPerBlock;  // plan tiles per plan workgroup
+constexpr int kPlanMaxBlocks = kPlanMaxTiles / kPlanBlockWaves;
+constexpr int kPlanPrefixLoads = kPlanMaxBlocks / kWave;  // earlier blocks per lane
+static_assert(kPlanMaxBlocks % kWave == 0, "plan blocks are read a wavefront at a time");
 constexpr int64_t kChunkTableSlack = 4096;  // chunk table holds M + this
 // Entries of one short tile staged per wavefront; short_max is capped at
 // kShortCap / R (R = row groups per wavefront) so that a tile of at least R
@@ -38,18 +42,19 @@ PlanShape plan_shape(int64_t M);
 // The plan lives in scratch memory that is kept per stream and reused by
 // every call on it.  Each word the plan publishes is tagged with the call's
 // epoch (upper 32 bits; the value in the lower 32), written and read with
-// device-coherent relaxed atomics; a reader waits until the tag equals the
+// device-coherent relaxed atomics; a reader polls until the tag equals the
 // current epoch.  Epochs start at 1 and grow by one per call, and the
 // scratch is zeroed when it is created, so no word needs clearing between
 // calls.
 struct PlanBuffers {
     uint64_t *counts;        // [4] n_medium, n_long, n_chunks, n_short
-    uint64_t *agg;           // [3 * kPlanMaxTiles] per tile: medium, long, chunks
+    uint64_t *agg;           // [3][kPlanMaxBlocks] per plan block: medium, long, chunks
     uint64_t *medium_rows;   // [M] rows with short_max < len <= medium_max
     uint64_t *long_row;      // [M] long rows, ascending
     uint64_t *long_first;    // [M] index of each long row's first chunk
     uint64_t *chunk_row;     // [chunk_cap] row of each chunk
     uint64_t *chunk_k;       // [chunk_cap] position of the chunk in its row
+    uint32_t *faults;        // items the product gave up waiting for (not tagged)
     int64_t chunk_cap;       // M + kChunkTableSlack
 };
 
@@ -90,13 +95,11 @@ struct WorkerArgs {
     uint32_t epoch;
 };
 
-// Enqueue the plan kernel and then the product kernel (the plan alone when
-// a.C is null).  The events (each may be null) are attached to the
-// dispatches: plan_start to the start of the plan kernel, work_start and
-// work_stop to the start and the end of the product kernel.
+// Enqueue a call: one launch that plans and computes the product (the plan
+// alone when a.C is null).  start/stop (each may be null) are attached to
+// the start and the end of that dispatch.
 hipError_t launch_worker(const WorkerConfig &cfg, const WorkerArgs &args,
-                         hipStream_t stream, hipEvent_t plan_start,
-                         hipEvent_t work_start, hipEvent_t work_stop);
+                         hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
 // Plain descriptors for the plan export.
 struct LongRow {

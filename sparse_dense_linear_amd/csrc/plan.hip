@@ -1,9 +1,9 @@
-// plan.hip -- the plan kernel, the launch sequence of a call, and the plan
-// export for tests.
+// plan.hip -- the plan on its own (for the plan export used by tests), the
+// launch of a call, and the plan export.
 //
-// A call is two launches on its stream: the plan kernel (plan_device.h: one
-// wavefront per tile) and the product kernel (worker.hip), which reads the
-// finished plan.
+// A call is one launch (worker.hip): its first workgroups compute the plan
+// (plan_device.h) and the rest compute the product.  The plan-only kernel
+// here runs the same plan blocks without a product.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -27,14 +27,10 @@ PlanShape plan_shape(int64_t M)
 
 namespace {
 
-// One wavefront per plan tile.
-__global__ __launch_bounds__(kBlock) void plan_kernel(WorkerArgs a)
+// One workgroup per plan block, one wavefront per plan tile.
+__global__ __launch_bounds__(kPlanBlockWaves * kWave) void plan_kernel(WorkerArgs a)
 {
-    __shared__ PlanLds lds[kWavesPerBlock];
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-    if (t >= a.shape.n_tiles)
-        return;
+    __shared__ PlanBlockLds lds;
     PlanCtx pc;
     pc.rowptr = a.rowptr;
     pc.C = a.C;
@@ -44,8 +40,8 @@ __global__ __launch_bounds__(kBlock) void plan_kernel(WorkerArgs a)
     pc.pb = a.plan;
     pc.sh = a.shape;
     pc.epoch = a.epoch;
-    pc.lane = lane;
-    plan_tile(pc, t, lds[threadIdx.x / kWave]);
+    pc.lane = threadIdx.x & (kWave - 1);
+    plan_block(pc, blockIdx.x, threadIdx.x / kWave, lds);
 }
 
 constexpr int kExportBlock = 256;
@@ -121,24 +117,19 @@ __global__ __launch_bounds__(kExportBlock) void plan_export_kernel(
 
 }  // namespace
 
-hipError_t launch_product(const WorkerConfig &cfg, const WorkerArgs &a,
-                          hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+hipError_t launch_call(const WorkerConfig &cfg, const WorkerArgs &a,
+                       hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 
 hipError_t launch_worker(const WorkerConfig &cfg, const WorkerArgs &a,
-                         hipStream_t stream, hipEvent_t plan_start,
-                         hipEvent_t work_start, hipEvent_t work_stop)
+                         hipStream_t stream, hipEvent_t start, hipEvent_t stop)
 {
-    if (a.shape.n_tiles > 0) {
-        const int64_t blocks = (a.shape.n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-        hipExtLaunchKernelGGL(plan_kernel, dim3((unsigned)blocks), dim3(kBlock), 0,
-                              stream, plan_start, nullptr, 0, a);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess)
-            return err;
-    }
-    if (a.C == nullptr)
-        return hipSuccess;  // plan only
-    return launch_product(cfg, a, stream, work_start, work_stop);
+    if (a.C != nullptr)
+        return launch_call(cfg, a, stream, start, stop);
+    // plan only
+    const int64_t blocks = (a.shape.n_tiles + kPlanBlockWaves - 1) / kPlanBlockWaves;
+    hipExtLaunchKernelGGL(plan_kernel, dim3((unsigned)blocks),
+                          dim3(kPlanBlockWaves * kWave), 0, stream, start, stop, 0, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_plan_export(const int32_t *rowptr, int64_t M, Thresholds th,

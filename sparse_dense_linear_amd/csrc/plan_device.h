@@ -15,25 +15,28 @@
 // several wavefronts (nnz split).  Its lists are a pure function of rowptr
 // and the thresholds: ascending row order, placed by prefix sums.
 //
-// The rows are cut into n_tiles tiles and one wavefront plans each tile:
-//   1. count the tile's medium rows, long rows and chunks and publish the
-//      three counts;
-//   2. add up the counts of all earlier tiles; a count that is not visible
-//      yet after a few polls is recomputed by this wavefront from rowptr
-//      (counting is idempotent), so no wavefront ever waits for another;
-//   3. write the tile's entries of the lists (for long rows: clear their C
-//      rows, then publish the rows and their chunks); the last tile also
-//      publishes the totals.
-// The product kernel runs after the plan kernel has ended, on the same
-// stream.  Every published word is tagged with the call's epoch (see
-// PlanBuffers), and the product skips an entry that does not carry it.
+// The rows are cut into n_tiles tiles, one wavefront per tile, and the
+// tiles are grouped kPlanBlockWaves to a workgroup (a plan block):
+//   1. each wavefront counts its tile's medium rows, long rows and chunks;
+//      the block adds them up in LDS and publishes the block's totals;
+//   2. one wavefront adds up the totals of all earlier blocks; a total that
+//      is not visible yet after a few polls is recomputed by this wavefront
+//      from rowptr (counting is idempotent), so no workgroup ever waits for
+//      another;
+//   3. each wavefront writes its tile's entries of the lists (for long
+//      rows: clear their C rows, then publish the rows and their chunks);
+//      the last block also publishes the totals.
+// Plan blocks are the first workgroups of the same launch as the product,
+// so the product reads the plan while it is being written: every published
+// word is tagged with the call's epoch (see PlanBuffers), and the product
+// polls for the tag of each word it needs.
 #pragma once
 
 #include "internal.h"
 
 namespace sdl {
 
-constexpr int kPlanPolls = 8;  // polls for an earlier tile's counts
+constexpr int kPlanPolls = 8;  // polls for an earlier block's counts
 
 // ------------------------------------------------------- tagged words
 
@@ -51,6 +54,19 @@ __device__ inline void tag_store(uint64_t *p, uint32_t epoch, uint32_t v)
 __device__ inline bool tag_is(uint64_t w, uint32_t epoch)
 {
     return (uint32_t)(w >> 32) == epoch;
+}
+
+// Wait until this wavefront's earlier global stores and atomics have
+// completed (vmcnt counts stores as well as loads on gfx9-family parts).
+// Device-coherent stores that have completed are visible device-wide, so a
+// tagged word stored after this point is only seen after them.  This is the
+// ordering step of the compiler's own release sequence without its L2
+// write-back, which only plain (non-coherent) stores need.
+__device__ inline void wait_stores_done()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt untouched
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // ------------------------------------------------------------ context
@@ -164,98 +180,170 @@ __device__ inline void count_tile(const PlanCtx &c, int64_t t, int *med,
     *chunks = wave_sum_i(ch);
 }
 
-// Sums of the counts of tiles 0 .. t-1.  Counts not visible after a few
-// polls are recomputed here.
-__device__ inline void prefix_before(const PlanCtx &c, int64_t t, int *med,
-                                     int *lng, int *chunks)
+// Counts of plan block b (its kPlanBlockWaves tiles), wave-uniform.
+__device__ inline void count_block(const PlanCtx &c, int64_t b, int *med,
+                                   int *lng, int *chunks)
 {
-    int sm = 0, sl = 0, sc = 0;
-    for (int64_t jb = 0; jb < t; jb += kWave) {
-        const int64_t j = jb + c.lane;
-        bool ready = j >= t;
-        int vm = 0, vl = 0, vc = 0;
-        for (int poll = 0; poll < kPlanPolls; ++poll) {
-            if (!ready) {
-                const uint64_t w0 = tag_load(c.pb.agg + 3 * j + 0);
-                const uint64_t w1 = tag_load(c.pb.agg + 3 * j + 1);
-                const uint64_t w2 = tag_load(c.pb.agg + 3 * j + 2);
-                if (tag_is(w0, c.epoch) && tag_is(w1, c.epoch) && tag_is(w2, c.epoch)) {
-                    vm = (int)(uint32_t)w0;
-                    vl = (int)(uint32_t)w1;
-                    vc = (int)(uint32_t)w2;
-                    ready = true;
-                }
-            }
-            if (__ballot(!ready) == 0)
-                break;
-            __builtin_amdgcn_s_sleep(1);
-        }
-        // recount whatever is still missing, one tile at a time
-        uint64_t missing = __ballot(!ready);
-        while (missing) {
-            const int l = __builtin_ctzll(missing);
-            missing &= missing - 1;
-            int m, lg, ch;
-            count_tile(c, jb + l, &m, &lg, &ch);
-            if (c.lane == l) {
-                vm = m;
-                vl = lg;
-                vc = ch;
-            }
-        }
-        sm += vm;
-        sl += vl;
-        sc += vc;
+    int m = 0, l = 0, ch = 0;
+    const int64_t t0 = b * kPlanBlockWaves;
+    for (int64_t t = t0; t < t0 + kPlanBlockWaves && t < c.sh.n_tiles; ++t) {
+        int tm, tl, tc;
+        count_tile(c, t, &tm, &tl, &tc);
+        m += tm;
+        l += tl;
+        ch += tc;
     }
-    *med = wave_sum_i(sm);
-    *lng = wave_sum_i(sl);
-    *chunks = wave_sum_i(sc);
+    *med = m;
+    *lng = l;
+    *chunks = ch;
 }
 
-// Plan tile t.  Never waits for another wavefront.
-__device__ inline void plan_tile(const PlanCtx &c, int64_t t, PlanLds &L)
+// Sums of the published counts of plan blocks 0 .. b-1: lane l reads
+// blocks l, l + 64, ... (all loads of a poll in flight together).  Counts
+// not visible after a few polls are recomputed here from rowptr.
+__device__ inline void block_prefix(const PlanCtx &c, int64_t b, int *med,
+                                    int *lng, int *chunks)
 {
-    int64_t r0, r1;
-    tile_range(c, t, &r0, &r1);
-    const bool one_round = r1 - r0 <= kPlanRoundRows;
-    LaneRows q = lane_rows(c, r0, r1);
-
-    // 1. publish this tile's counts
-    int own_med, own_long, own_chunks;
-    if (one_round) {
-        int m = 0, l = 0, ch = 0;
+    int vm = 0, vl = 0, vc = 0;
+    if (b > 0) {
+        uint32_t need = 0;  // bit i: block lane + 64 i is still to be read
 #pragma unroll
-        for (int k = 0; k < kPlanLaneRows; ++k) {
-            m += q.rc[k].medium;
-            l += q.rc[k].lng;
-            ch += q.rc[k].chunks;
+        for (int i = 0; i < kPlanPrefixLoads; ++i)
+            need |= (c.lane + kWave * i < b) ? 1u << i : 0u;
+        for (int poll = 0; poll < kPlanPolls && __ballot(need != 0) != 0; ++poll) {
+            if (poll > 0)
+                __builtin_amdgcn_s_sleep(2);
+            uint64_t wd[kPlanPrefixLoads][3];
+#pragma unroll
+            for (int i = 0; i < kPlanPrefixLoads; ++i) {
+                const int64_t jb = c.lane + kWave * i;
+                const int64_t jj = jb < b ? jb : b - 1;
+#pragma unroll
+                for (int k = 0; k < 3; ++k)
+                    wd[i][k] = tag_load(c.pb.agg + k * kPlanMaxBlocks + jj);
+            }
+#pragma unroll
+            for (int i = 0; i < kPlanPrefixLoads; ++i) {
+                const bool got = ((need >> i) & 1u) && tag_is(wd[i][0], c.epoch) &&
+                                 tag_is(wd[i][1], c.epoch) && tag_is(wd[i][2], c.epoch);
+                if (got) {
+                    vm += (int)(uint32_t)wd[i][0];
+                    vl += (int)(uint32_t)wd[i][1];
+                    vc += (int)(uint32_t)wd[i][2];
+                    need &= ~(1u << i);
+                }
+            }
         }
-        own_med = wave_sum_i(m);
-        own_long = wave_sum_i(l);
-        own_chunks = wave_sum_i(ch);
-    } else {
-        count_tile(c, t, &own_med, &own_long, &own_chunks);
+#pragma unroll
+        for (int i = 0; i < kPlanPrefixLoads; ++i) {
+            uint64_t missing = __ballot((need >> i) & 1u);
+            while (missing) {
+                const int l = __builtin_ctzll(missing);
+                missing &= missing - 1;
+                int m, lg, ch;
+                count_block(c, l + (int64_t)kWave * i, &m, &lg, &ch);
+                if (c.lane == l) {
+                    vm += m;
+                    vl += lg;
+                    vc += ch;
+                }
+            }
+        }
+    }
+    *med = wave_sum_i(vm);
+    *lng = wave_sum_i(vl);
+    *chunks = wave_sum_i(vc);
+}
+
+// Block-shared state of the plan kernel.
+struct PlanBlockLds {
+    PlanLds wave[kPlanBlockWaves];
+    int cnt[3][kPlanBlockWaves];   // per tile: medium, long, chunks
+    int off[3];                    // offsets of this block in the lists
+};
+
+// Plan block b: wavefront w of the block plans tile b * kPlanBlockWaves + w.
+// Called by every thread of the block (it synchronises the block).
+__device__ inline void plan_block(const PlanCtx &c, int64_t b, int w, PlanBlockLds &S)
+{
+    const int64_t t = b * kPlanBlockWaves + w;
+    const bool active = t < c.sh.n_tiles;
+    int64_t r0 = 0, r1 = 0;
+    LaneRows q{};
+    bool one_round = false;
+
+    // 1. this tile's counts, gathered in LDS
+    int own_med = 0, own_long = 0, own_chunks = 0;
+    if (active) {
+        tile_range(c, t, &r0, &r1);
+        one_round = r1 - r0 <= kPlanRoundRows;
+        if (one_round) {
+            q = lane_rows(c, r0, r1);
+            int m = 0, l = 0, ch = 0;
+#pragma unroll
+            for (int k = 0; k < kPlanLaneRows; ++k) {
+                m += q.rc[k].medium;
+                l += q.rc[k].lng;
+                ch += q.rc[k].chunks;
+            }
+            own_med = wave_sum_i(m);
+            own_long = wave_sum_i(l);
+            own_chunks = wave_sum_i(ch);
+        } else {
+            count_tile(c, t, &own_med, &own_long, &own_chunks);
+        }
     }
     if (c.lane == 0) {
-        tag_store(c.pb.agg + 3 * t + 0, c.epoch, (uint32_t)own_med);
-        tag_store(c.pb.agg + 3 * t + 1, c.epoch, (uint32_t)own_long);
-        tag_store(c.pb.agg + 3 * t + 2, c.epoch, (uint32_t)own_chunks);
+        S.cnt[0][w] = own_med;
+        S.cnt[1][w] = own_long;
+        S.cnt[2][w] = own_chunks;
     }
+    __syncthreads();
 
-    // 2. offsets from the earlier tiles
-    int med_off, long_off, chunk_off;
-    prefix_before(c, t, &med_off, &long_off, &chunk_off);
-    if (t == c.sh.n_tiles - 1 && c.lane == 0) {
-        const int n_med = med_off + own_med, n_long = long_off + own_long;
-        tag_store(c.pb.counts + 0, c.epoch, (uint32_t)n_med);
-        tag_store(c.pb.counts + 1, c.epoch, (uint32_t)n_long);
-        tag_store(c.pb.counts + 2, c.epoch, (uint32_t)(chunk_off + own_chunks));
-        tag_store(c.pb.counts + 3, c.epoch, (uint32_t)(c.M - n_med - n_long));
+    // 2. block totals, this tile's place in the block, the block's place
+    int tot[3] = {0, 0, 0}, pre[3] = {0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < kPlanBlockWaves; ++i) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int v = S.cnt[k][i];
+            tot[k] += v;
+            pre[k] += i < w ? v : 0;
+        }
     }
+    if (w == 0) {
+        if (c.lane == 0) {
+            tag_store(c.pb.agg + b, c.epoch, (uint32_t)tot[0]);
+            tag_store(c.pb.agg + kPlanMaxBlocks + b, c.epoch, (uint32_t)tot[1]);
+            tag_store(c.pb.agg + 2 * kPlanMaxBlocks + b, c.epoch, (uint32_t)tot[2]);
+        }
+        int bm, bl, bc;
+        block_prefix(c, b, &bm, &bl, &bc);
+        if (c.lane == 0) {
+            S.off[0] = bm;
+            S.off[1] = bl;
+            S.off[2] = bc;
+            if ((b + 1) * kPlanBlockWaves >= c.sh.n_tiles) {
+                // last block: the totals of the whole plan
+                const int n_med = bm + tot[0], n_long = bl + tot[1];
+                tag_store(c.pb.counts + 0, c.epoch, (uint32_t)n_med);
+                tag_store(c.pb.counts + 1, c.epoch, (uint32_t)n_long);
+                tag_store(c.pb.counts + 2, c.epoch, (uint32_t)(bc + tot[2]));
+                tag_store(c.pb.counts + 3, c.epoch, (uint32_t)(c.M - n_med - n_long));
+            }
+        }
+    }
+    __syncthreads();
+    if (!active)
+        return;
+    int med_off = S.off[0] + pre[0];
+    int long_off = S.off[1] + pre[1];
+    int chunk_off = S.off[2] + pre[2];
+    PlanLds &L = S.wave[w];
 
     // 3. the tile's entries, a round of kPlanRoundRows rows at a time
     for (int64_t base = r0; base < r1; base += kPlanRoundRows) {
-        if (base != r0)
+        if (base != r0 || !one_round)
             q = lane_rows(c, base, r1);
         int my_med = 0, my_long = 0, my_chunks = 0;
 #pragma unroll
@@ -285,12 +373,19 @@ __device__ inline void plan_tile(const PlanCtx &c, int64_t t, PlanLds &L)
         if (round_long > 0) {
             // Clear the C rows of this round's long rows (the product adds
             // their chunks into them with atomics).
+            // The product (same launch) adds into these rows with device
+            // atomics as soon as their chunks are published, so the zeros
+            // must have reached device scope first: they are written as
+            // device-coherent atomic stores, and the chunk entries are
+            // published only after those stores have completed.
             if (c.C != nullptr) {
                 for (int x = 0; x < round_long; ++x) {
                     float *crow = c.C + (int64_t)L.row[x] * c.N;
                     for (int64_t n = c.lane; n < c.N; n += kWave)
-                        crow[n] = 0.0f;
+                        __hip_atomic_store(crow + n, 0.0f, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
                 }
+                wait_stores_done();
             }
             for (int x = c.lane; x < round_long; x += kWave) {
                 tag_store(c.pb.long_row + long_off + x, c.epoch, (uint32_t)L.row[x]);

@@ -25,11 +25,13 @@
 //   * colind/vals of the entries being worked on are staged in LDS, loaded
 //     once with coalesced loads and then read (as broadcasts) by the lanes
 //     that cover the N columns.
-//   * Three kinds of work item, all handled by one grid-stride kernel:
+//   * One launch per call: the first workgroups compute the plan
+//     (plan_device.h) while the others start on short tiles; three kinds
+//     of work item, all handled by one grid-stride loop:
 //       long chunk  (row, p0, p1) from the plan: the R groups split the
 //                   chunk's entries, their partial rows are summed by
 //                   butterfly shuffles, and group 0 adds the result to C
-//                   with fp32 atomics (the row was zeroed by the plan);
+//                   with fp32 atomics (the row was cleared by the plan);
 //       medium row  from the plan: as a chunk over the whole row, but the
 //                   result is stored, not added;
 //       short tile  a block of T consecutive rows in natural order.  The
@@ -549,23 +551,76 @@ __device__ inline bool counts_ready(const WorkerArgs &a, int64_t *n_med,
     return true;
 }
 
-// The product, after the plan kernel: every wavefront takes items w, w+W,
-// w+2W, ... of the list [long-row chunks | medium rows | short tiles].  A
-// plan entry that does not carry this call's epoch (the plan gave up) is
-// skipped, never waited for.
-template <class S>
-__global__ __launch_bounds__(kBlock) void worker_kernel(WorkerArgs a,
-                                                        int64_t n_tiles,
-                                                        int passes,
-                                                        int64_t total_waves)
+// Polls for a plan word.  The plan blocks are the first workgroups of the
+// launch, each XCD starts its workgroups in order, and a plan block never
+// waits, so the plan is running (and finishes) whenever a product
+// wavefront runs; the bound (about a second) only guarantees that every
+// wavefront exits.
+constexpr int kWaitPolls = 1 << 19;
+
+template <class Ready>
+__device__ inline bool wait_for(Ready ready)
 {
-    __shared__ WaveStage stage[kWavesPerBlock];
+    for (int i = 0; i < kWaitPolls; ++i) {
+        if (ready())
+            return true;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return false;
+}
+
+// An item whose plan entry never became visible is left undone and counted.
+__device__ inline void note_fault(const WorkerArgs &a, int lane)
+{
+    if (lane == 0)
+        atomicAdd(a.plan.faults, 1u);
+}
+
+// One launch per call.  Workgroups [0, plan_blocks) plan (plan_device.h);
+// [plan_blocks, plan_grid) pad the plan part to a multiple of 8 workgroups
+// and exit; the rest run the product.  Product wavefront w takes items w,
+// w+W, w+2W, ... of the list
+//     [short tiles 0..F-1 | long-row chunks | medium rows | short tiles F..]
+// with W product wavefronts and F = min(W, short tiles): every wavefront
+// starts on a short tile, which needs no plan, while the plan is written.
+template <class S>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4)))
+void call_kernel(WorkerArgs a,
+                                                      int64_t n_short_tiles,
+                                                      int passes,
+                                                      int64_t plan_blocks,
+                                                      int64_t plan_grid,
+                                                      int64_t total_waves)
+{
+    __shared__ union {
+        WaveStage stage[kWavesPerBlock];
+        PlanBlockLds plan;
+    } lds;
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = threadIdx.x / kWave;
+    if ((int64_t)blockIdx.x < plan_grid) {
+        if ((int64_t)blockIdx.x < plan_blocks) {
+            PlanCtx pc;
+            pc.rowptr = a.rowptr;
+            pc.C = a.C;
+            pc.M = a.M;
+            pc.N = a.N;
+            pc.th = a.th;
+            pc.pb = a.plan;
+            pc.sh = a.shape;
+            pc.epoch = a.epoch;
+            pc.lane = lane;
+            plan_block(pc, blockIdx.x, wid, lds.plan);
+        }
+        return;
+    }
+
     const int g = lane / S::G;
     const int j = lane % S::G;
-    WaveStage &ws = stage[wid];
-    const int64_t w = xcd_logical_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wid;
+    WaveStage &ws = lds.stage[wid];
+    // plan_grid is a multiple of 8, so product block b runs on XCD b % 8
+    const int64_t w = xcd_logical_block((int64_t)blockIdx.x - plan_grid,
+                                        (int64_t)gridDim.x - plan_grid) * kWavesPerBlock + wid;
 
     const uint32_t row_bytes = (uint32_t)(a.N * S::ESZ);
     BSrc src;
@@ -575,19 +630,37 @@ __global__ __launch_bounds__(kBlock) void worker_kernel(WorkerArgs a,
             const_cast<void *>(a.B), (short)0,
             (int)(uint32_t)(a.K * a.N * S::ESZ), kBufferWord3);
 
+    const int64_t first = n_short_tiles < total_waves ? n_short_tiles : total_waves;
+    int64_t item = w;
+    if (item < first) {
+        do_short_tile<S>(a, ws, lane, g, j, item, passes, src, row_bytes);
+        item += total_waves;
+    }
+
     int64_t n_med = 0, n_long = 0, n_ch = 0;
-    if (!counts_ready(a, &n_med, &n_long, &n_ch))
+    if (!wait_for([&]() { return counts_ready(a, &n_med, &n_long, &n_ch); })) {
+        note_fault(a, lane);
         n_med = n_long = n_ch = 0;
-    const int64_t n_items = n_ch + n_med + n_tiles;
-    for (int64_t item = w; item < n_items; item += total_waves) {
-        int64_t row, p0, p1;
-        if (item < n_ch) {
-            if (chunk_ready(a, item, n_long, &row, &p0, &p1))
+    }
+    const int64_t n_items = n_short_tiles + n_ch + n_med;
+    for (; item < n_items; item += total_waves) {
+        const int64_t x = item - first;
+        int64_t row = 0, p0 = 0, p1 = 0;
+        if (x < n_ch) {
+            // The row was cleared (device-coherent stores, completed)
+            // before its chunk was published; the atomic adds address it
+            // through the published row, so they come after the clearing.
+            if (wait_for([&]() { return chunk_ready(a, x, n_long, &row, &p0, &p1); })) {
                 do_range<S, true>(a, ws, lane, g, j, row, p0, p1, src, row_bytes);
-        } else if (item < n_ch + n_med) {
-            if (medium_ready(a, item - n_ch, &row))
+            } else {
+                note_fault(a, lane);
+            }
+        } else if (x < n_ch + n_med) {
+            if (wait_for([&]() { return medium_ready(a, x - n_ch, &row); }))
                 do_range<S, false>(a, ws, lane, g, j, row, a.rowptr[row],
                                    a.rowptr[row + 1], src, row_bytes);
+            else
+                note_fault(a, lane);
         } else {
             do_short_tile<S>(a, ws, lane, g, j, item - n_ch - n_med, passes,
                              src, row_bytes);
@@ -607,7 +680,7 @@ hipError_t launch_shape(const WorkerArgs &a, hipStream_t stream,
             err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (err == hipSuccess)
             err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, reinterpret_cast<const void *>(worker_kernel<S>), kBlock, 0);
+                &per_cu, reinterpret_cast<const void *>(call_kernel<S>), kBlock, 0);
         if (err != hipSuccess)
             return err;
         resident_blocks = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
@@ -625,14 +698,16 @@ hipError_t launch_shape(const WorkerArgs &a, hipStream_t stream,
     int64_t passes = a.M / ((int64_t)S::R * resident_waves);
     passes = passes < 1 ? 1 : (passes > max_passes ? max_passes : passes);
     const int64_t tile = passes * S::R;
-    const int64_t n_tiles = (a.M + tile - 1) / tile;
-    // The number of long-row chunks is known only on the device, so the
-    // grid is every block that fits at once; waves without work exit after
-    // reading the plan counts.
-    const int64_t blocks = resident_blocks;
-    hipExtLaunchKernelGGL(worker_kernel<S>, dim3((unsigned)blocks), dim3(kBlock),
-                          0, stream, start, stop, 0, a, n_tiles, (int)passes,
-                          blocks * kWavesPerBlock);
+    const int64_t n_short_tiles = (a.M + tile - 1) / tile;
+    // Plan workgroups first (padded to a multiple of the 8 XCDs), then one
+    // product workgroup per resident slot: the number of long-row chunks is
+    // known only on the device, so the product part is a grid-stride loop.
+    const int64_t plan_blocks = (a.shape.n_tiles + kPlanBlockWaves - 1) / kPlanBlockWaves;
+    const int64_t plan_grid = (plan_blocks + 7) / 8 * 8;
+    const int64_t blocks = plan_grid + resident_blocks;
+    hipExtLaunchKernelGGL(call_kernel<S>, dim3((unsigned)blocks), dim3(kBlock),
+                          0, stream, start, stop, 0, a, n_short_tiles, (int)passes,
+                          plan_blocks, plan_grid, (int64_t)resident_blocks * kWavesPerBlock);
     return hipGetLastError();
 }
 
@@ -703,8 +778,8 @@ hipError_t launch_dtype(const WorkerConfig &cfg, const WorkerArgs &a,
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_product(const WorkerConfig &cfg, const WorkerArgs &a,
-                          hipStream_t s, hipEvent_t e0, hipEvent_t e1)
+hipError_t launch_call(const WorkerConfig &cfg, const WorkerArgs &a,
+                       hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
     // B is addressed through a buffer resource (32-bit byte offsets) when it
     // is below 4 GiB, otherwise through flat 64-bit addresses.

@@ -43,6 +43,7 @@ def run_gpu(p, tuning=None, fill=float("nan")):
     C = torch.full((p.M * p.N,), fill, dtype=torch.float32, device="cuda")
     call(p, rowptr, colind, vals, B, C, tuning=tuning)
     torch.cuda.synchronize()
+    assert sdl.stream_faults() == 0, "a product wavefront gave up waiting for the plan"
     return C.cpu().numpy().reshape(p.M, p.N)
 
 

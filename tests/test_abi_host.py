@@ -25,7 +25,8 @@ def test_header_declares_entry_points():
     names = header_functions()
     for must in ("spmm_csr_f32", "spmm_csr_bf16in_f32acc", "spmm_csr_tuned",
                  "spmm_resolve_tuning", "spmm_plan_export", "spmm_status_string",
-                 "spmm_last_error", "spmm_timing_enable", "spmm_timing_read"):
+                 "spmm_last_error", "spmm_timing_enable", "spmm_timing_read",
+                 "spmm_stream_faults"):
         assert must in names
 
 

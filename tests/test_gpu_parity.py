@@ -201,6 +201,35 @@ PLAN_CASES = [
 ]
 
 
+def _lengths_rowptr(M, seed, dmax=8192, alpha=2.1, base=0):
+    """rowptr only, power-law row lengths (the plan reads nothing else)."""
+    rng = np.random.default_rng(seed)
+    d = np.arange(1, dmax + 1, dtype=np.float64)
+    cdf = np.cumsum(d ** -alpha)
+    lens = np.searchsorted(cdf / cdf[-1], rng.random(M)) + 1
+    lens[rng.random(M) < 0.05] = 0
+    return np.concatenate([[base], base + np.cumsum(lens)]).astype(np.int32)
+
+
+# M chosen so that plan tiles hold one round (262144), several rounds with
+# a ragged tail (600001), and a last plan block with a single tile (262145).
+PLAN_ROWPTR_CASES = [(262144, 0, None), (600001, 7, None), (262145, 0, sdl.Tuning(4, 40, 17))]
+
+
+@pytest.mark.parametrize("M,base,tuning", PLAN_ROWPTR_CASES,
+                         ids=[f"M{c[0]}" for c in PLAN_ROWPTR_CASES])
+def test_plan_bit_exact_many_blocks(M, base, tuning):
+    rp = _lengths_rowptr(M, seed=M % 97, base=base)
+    t = sdl.resolve_tuning(0, 64, tuning)
+    got = sdl.plan_export(torch.from_numpy(rp).cuda(), t)
+    want = oracle.plan_ref(rp, t.short_max, t.medium_max, t.chunk_nnz)
+    for k in ("n_short", "n_medium", "n_long", "n_chunks"):
+        assert got[k] == want[k], k
+    assert np.array_equal(got["medium_rows"], want["medium_rows"])
+    assert np.array_equal(got["long_rows"], want["long_rows"])
+    assert np.array_equal(got["chunks"], want["chunks"])
+
+
 @pytest.mark.parametrize("name,make,tuning", PLAN_CASES, ids=[c[0] for c in PLAN_CASES])
 def test_plan_bit_exact(name, make, tuning):
     p = make()
