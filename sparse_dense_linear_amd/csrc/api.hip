@@ -128,7 +128,7 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 // PlanBuffers).  The block is zeroed when created; words are tagged with a
 // per-call epoch, so a block can serve calls of any M up to its size.
 struct ScratchLayout {
-    int64_t counts, faults, agg, medium_rows, long_row,
+    int64_t counts, faults, queues, agg, medium_rows, long_row,
         long_first, chunk_row, chunk_k, total;
     int64_t chunk_cap;
 };
@@ -141,6 +141,8 @@ ScratchLayout scratch_layout(int64_t M)
     off = align_up(off + 4 * 8, 256);
     l.faults = off;
     off = align_up(off + 4, 256);
+    l.queues = off;
+    off = align_up(off + 4 * 2 * kQueues * kQueueStride, 256);
     l.agg = off;
     off = align_up(off + 8 * 3 * kPlanMaxBlocks, 256);
     l.medium_rows = off;
@@ -169,6 +171,7 @@ PlanBuffers carve(char *base, const ScratchLayout &l)
     b.chunk_row = (uint64_t *)(base + l.chunk_row);
     b.chunk_k = (uint64_t *)(base + l.chunk_k);
     b.faults = (uint32_t *)(base + l.faults);
+    b.queues = (uint32_t *)(base + l.queues);
     b.chunk_cap = l.chunk_cap;
     return b;
 }

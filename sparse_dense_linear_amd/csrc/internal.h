@@ -18,6 +18,10 @@ constexpr int kPlanMaxBlocks = kPlanMaxTiles / kPlanBlockWaves;
 constexpr int kPlanPrefixLoads = kPlanMaxBlocks / kWave;  // earlier blocks per lane
 static_assert(kPlanMaxBlocks % kWave == 0, "plan blocks are read a wavefront at a time");
 constexpr int64_t kChunkTableSlack = 4096;  // chunk table holds M + this
+// Work queues of the product: kQueues grab counters per call, kQueueStride
+// 32-bit words apart (256 bytes, so they sit in different memory channels).
+constexpr int kQueues = 32;
+constexpr int kQueueStride = 64;
 // Entries of one short tile staged per wavefront; short_max is capped at
 // kShortCap / R (R = row groups per wavefront) so that a tile of at least R
 // rows always fits.
@@ -55,6 +59,9 @@ struct PlanBuffers {
     uint64_t *chunk_row;     // [chunk_cap] row of each chunk
     uint64_t *chunk_k;       // [chunk_cap] position of the chunk in its row
     uint32_t *faults;        // items the product gave up waiting for (not tagged)
+    uint32_t *queues;        // [2][kQueues * kQueueStride] grab counters: a call
+                             // uses set epoch & 1 and clears the other set for
+                             // the next call (not tagged)
     int64_t chunk_cap;       // M + kChunkTableSlack
 };
 

@@ -576,21 +576,50 @@ __device__ inline void note_fault(const WorkerArgs &a, int lane)
         atomicAdd(a.plan.faults, 1u);
 }
 
-// One launch per call.  Workgroups [0, plan_blocks) plan (plan_device.h);
-// [plan_blocks, plan_grid) pad the plan part to a multiple of 8 workgroups
-// and exit; the rest run the product.  Product wavefront w takes items w,
-// w+W, w+2W, ... of the list
-//     [short tiles 0..F-1 | long-row chunks | medium rows | short tiles F..]
-// with W product wavefronts and F = min(W, short tiles): every wavefront
-// starts on a short tile, which needs no plan, while the plan is written.
+// One dynamic item: [0, n_ch) long-row chunks, then short tiles
+// first .. n_short_tiles-1, then medium rows (heaviest kinds first).
+template <class S>
+__device__ inline void do_item(const WorkerArgs &a, WaveStage &ws, int lane,
+                               int g, int j, int64_t d, int64_t first,
+                               int64_t n_short_tiles, int64_t n_ch,
+                               int64_t n_long, int passes, const BSrc &src,
+                               uint32_t row_bytes)
+{
+    int64_t row = 0, p0 = 0, p1 = 0;
+    const int64_t n_rest = n_short_tiles - first;
+    if (d < n_ch) {
+        // The row was cleared (device-coherent stores, completed) before its
+        // chunk was published; the atomic adds address it through the
+        // published row, so they come after the clearing.
+        if (wait_for([&]() { return chunk_ready(a, d, n_long, &row, &p0, &p1); }))
+            do_range<S, true>(a, ws, lane, g, j, row, p0, p1, src, row_bytes);
+        else
+            note_fault(a, lane);
+    } else if (d < n_ch + n_rest) {
+        do_short_tile<S>(a, ws, lane, g, j, first + (d - n_ch), passes, src, row_bytes);
+    } else {
+        if (wait_for([&]() { return medium_ready(a, d - n_ch - n_rest, &row); }))
+            do_range<S, false>(a, ws, lane, g, j, row, a.rowptr[row],
+                               a.rowptr[row + 1], src, row_bytes);
+        else
+            note_fault(a, lane);
+    }
+}
+
+// One launch per call, sized to the workgroups that fit at once.
+// Workgroups [0, plan_blocks) first compute the plan (plan_device.h);
+// [plan_blocks, plan_grid) pad that part to a multiple of the 8 XCDs.
+// Product workgroups (the rest) start with one short tile each (static:
+// logical product wavefront w takes tile w, for w < first), which needs no
+// plan.  Then every wavefront, the planners included, takes the remaining
+// items from kQueues work queues: queue q hands out items q, q + kQueues,
+// ... in the order [long-row chunks | short tiles | medium rows], so every
+// queue holds the same mix, heaviest items first, and a wavefront that
+// started late or drew slow items simply takes fewer.
 template <class S>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4)))
-void call_kernel(WorkerArgs a,
-                                                      int64_t n_short_tiles,
-                                                      int passes,
-                                                      int64_t plan_blocks,
-                                                      int64_t plan_grid,
-                                                      int64_t total_waves)
+void call_kernel(WorkerArgs a, int64_t n_short_tiles, int passes,
+                 int64_t plan_blocks, int64_t plan_grid, int64_t static_waves)
 {
     __shared__ union {
         WaveStage stage[kWavesPerBlock];
@@ -598,7 +627,9 @@ void call_kernel(WorkerArgs a,
     } lds;
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = threadIdx.x / kWave;
-    if ((int64_t)blockIdx.x < plan_grid) {
+    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wid;
+    const bool planner = (int64_t)blockIdx.x < plan_grid;
+    if (planner) {
         if ((int64_t)blockIdx.x < plan_blocks) {
             PlanCtx pc;
             pc.rowptr = a.rowptr;
@@ -612,16 +643,17 @@ void call_kernel(WorkerArgs a,
             pc.lane = lane;
             plan_block(pc, blockIdx.x, wid, lds.plan);
         }
-        return;
+        // Clear the queue counters of the next call on this stream (the
+        // previous call, which used them, has ended).
+        if (blockIdx.x == 0 && wid == 0 && lane < kQueues)
+            a.plan.queues[((a.epoch + 1) & 1) * kQueues * kQueueStride +
+                          lane * kQueueStride] = 0;
+        __syncthreads();  // the block's LDS now serves the product
     }
 
     const int g = lane / S::G;
     const int j = lane % S::G;
     WaveStage &ws = lds.stage[wid];
-    // plan_grid is a multiple of 8, so product block b runs on XCD b % 8
-    const int64_t w = xcd_logical_block((int64_t)blockIdx.x - plan_grid,
-                                        (int64_t)gridDim.x - plan_grid) * kWavesPerBlock + wid;
-
     const uint32_t row_bytes = (uint32_t)(a.N * S::ESZ);
     BSrc src;
     src.base = (const char *)a.B;
@@ -630,11 +662,14 @@ void call_kernel(WorkerArgs a,
             const_cast<void *>(a.B), (short)0,
             (int)(uint32_t)(a.K * a.N * S::ESZ), kBufferWord3);
 
-    const int64_t first = n_short_tiles < total_waves ? n_short_tiles : total_waves;
-    int64_t item = w;
-    if (item < first) {
-        do_short_tile<S>(a, ws, lane, g, j, item, passes, src, row_bytes);
-        item += total_waves;
+    const int64_t first = n_short_tiles < static_waves ? n_short_tiles : static_waves;
+    if (!planner) {
+        // plan_grid is a multiple of 8, so product block b runs on XCD b % 8
+        const int64_t w = xcd_logical_block((int64_t)blockIdx.x - plan_grid,
+                                            (int64_t)gridDim.x - plan_grid) *
+                              kWavesPerBlock + wid;
+        if (w < first)
+            do_short_tile<S>(a, ws, lane, g, j, w, passes, src, row_bytes);
     }
 
     int64_t n_med = 0, n_long = 0, n_ch = 0;
@@ -642,29 +677,22 @@ void call_kernel(WorkerArgs a,
         note_fault(a, lane);
         n_med = n_long = n_ch = 0;
     }
-    const int64_t n_items = n_short_tiles + n_ch + n_med;
-    for (; item < n_items; item += total_waves) {
-        const int64_t x = item - first;
-        int64_t row = 0, p0 = 0, p1 = 0;
-        if (x < n_ch) {
-            // The row was cleared (device-coherent stores, completed)
-            // before its chunk was published; the atomic adds address it
-            // through the published row, so they come after the clearing.
-            if (wait_for([&]() { return chunk_ready(a, x, n_long, &row, &p0, &p1); })) {
-                do_range<S, true>(a, ws, lane, g, j, row, p0, p1, src, row_bytes);
-            } else {
-                note_fault(a, lane);
-            }
-        } else if (x < n_ch + n_med) {
-            if (wait_for([&]() { return medium_ready(a, x - n_ch, &row); }))
-                do_range<S, false>(a, ws, lane, g, j, row, a.rowptr[row],
-                                   a.rowptr[row + 1], src, row_bytes);
-            else
-                note_fault(a, lane);
-        } else {
-            do_short_tile<S>(a, ws, lane, g, j, item - n_ch - n_med, passes,
-                             src, row_bytes);
-        }
+    const int64_t n_dyn = n_ch + (n_short_tiles - first) + n_med;
+    const int64_t q = gw % kQueues;
+    uint32_t *ctr = a.plan.queues + ((a.epoch & 1) * kQueues + q) * kQueueStride;
+    // Lane 0 holds the next grabbed index; it is read (and waited for) only
+    // at the top of the next round, so the grab overlaps the current item.
+    uint32_t next = 0;
+    if (lane == 0)
+        next = atomicAdd(ctr, 1u);
+    for (;;) {
+        const int64_t d = q + (int64_t)kQueues * __builtin_amdgcn_readfirstlane(next);
+        if (d >= n_dyn)
+            break;
+        if (lane == 0)
+            next = atomicAdd(ctr, 1u);
+        do_item<S>(a, ws, lane, g, j, d, first, n_short_tiles, n_ch, n_long,
+                   passes, src, row_bytes);
     }
 }
 
@@ -685,29 +713,32 @@ hipError_t launch_shape(const WorkerArgs &a, hipStream_t stream,
             return err;
         resident_blocks = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
     }
+    // Plan workgroups first (padded to a multiple of the 8 XCDs), product
+    // workgroups in the remaining slots, so that every workgroup starts at
+    // once.
+    const int64_t plan_blocks = (a.shape.n_tiles + kPlanBlockWaves - 1) / kPlanBlockWaves;
+    const int64_t plan_grid = (plan_blocks + 7) / 8 * 8;
+    int64_t product_blocks = resident_blocks - plan_grid;
+    if (product_blocks < 8)
+        product_blocks = 8;
+    const int64_t product_waves = product_blocks * kWavesPerBlock;
     // Short tiles: P rows per group (T = P*R rows, at most 64), at most 8,
     // small enough that the staged entries fit (T * short_max <= kShortCap),
-    // and fewer when M is too small to give every resident wavefront a tile.
-    const int64_t resident_waves = (int64_t)resident_blocks * kWavesPerBlock;
+    // and fewer when M is too small to give every product wavefront a tile.
     const int64_t smax = a.th.short_max > 1 ? a.th.short_max : 1;
     int64_t max_passes = kWave / S::R < 8 ? kWave / S::R : 8;
     if (max_passes > kShortCap / (S::R * smax))
         max_passes = kShortCap / (S::R * smax);
     if (max_passes < 1)
         return hipErrorInvalidValue;  // short_max above the group capacity
-    int64_t passes = a.M / ((int64_t)S::R * resident_waves);
+    int64_t passes = a.M / ((int64_t)S::R * product_waves);
     passes = passes < 1 ? 1 : (passes > max_passes ? max_passes : passes);
     const int64_t tile = passes * S::R;
     const int64_t n_short_tiles = (a.M + tile - 1) / tile;
-    // Plan workgroups first (padded to a multiple of the 8 XCDs), then one
-    // product workgroup per resident slot: the number of long-row chunks is
-    // known only on the device, so the product part is a grid-stride loop.
-    const int64_t plan_blocks = (a.shape.n_tiles + kPlanBlockWaves - 1) / kPlanBlockWaves;
-    const int64_t plan_grid = (plan_blocks + 7) / 8 * 8;
-    const int64_t blocks = plan_grid + resident_blocks;
+    const int64_t blocks = plan_grid + product_blocks;
     hipExtLaunchKernelGGL(call_kernel<S>, dim3((unsigned)blocks), dim3(kBlock),
                           0, stream, start, stop, 0, a, n_short_tiles, (int)passes,
-                          plan_blocks, plan_grid, (int64_t)resident_blocks * kWavesPerBlock);
+                          plan_blocks, plan_grid, product_waves);
     return hipGetLastError();
 }
 
