@@ -20,7 +20,7 @@ static_assert(kPlanMaxBlocks % kWave == 0, "plan blocks are read a wavefront at 
 constexpr int64_t kChunkTableSlack = 4096;  // chunk table holds M + this
 // Work queues of the product: kQueues grab counters per call, kQueueStride
 // 32-bit words apart (256 bytes, so they sit in different memory channels).
-constexpr int kQueues = 32;
+constexpr int kQueues = 64;
 constexpr int kQueueStride = 64;
 // Entries of one short tile staged per wavefront; short_max is capped at
 // kShortCap / R (R = row groups per wavefront) so that a tile of at least R

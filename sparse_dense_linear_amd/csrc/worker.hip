@@ -449,11 +449,10 @@ __device__ void do_range(const WorkerArgs &a, WaveStage &ws, int lane, int g,
 // g*P .. g*P+P-1 of the tile.
 template <class S>
 __device__ void do_short_tile(const WorkerArgs &a, WaveStage &ws, int lane,
-                              int g, int j, int64_t t, int P,
+                              int g, int j, int64_t r0, int P,
                               const BSrc &src, uint32_t row_bytes)
 {
     const int T = P * S::R;
-    const int64_t r0 = t * (int64_t)T;
     const int64_t r = r0 + lane;
     const bool in_tile = lane < T && r < a.M;
     int32_t s = 0, len = 0;
@@ -576,17 +575,29 @@ __device__ inline void note_fault(const WorkerArgs &a, int lane)
         atomicAdd(a.plan.faults, 1u);
 }
 
-// One dynamic item: [0, n_ch) long-row chunks, then short tiles
-// first .. n_short_tiles-1, then medium rows (heaviest kinds first).
+// How the product's work is cut, fixed by the host for one launch.
+struct ProductShape {
+    int passes;            // P of the static short tiles (T = P*R rows)
+    int dyn_passes;        // P of the short tiles handed out by the queues
+    int64_t first;         // static short tiles (one per product wavefront)
+    int64_t rows_static;   // rows [0, rows_static) are in static tiles
+    int64_t n_dyn_tiles;   // short tiles over rows [rows_static, M)
+    int64_t plan_blocks;   // workgroups that compute the plan
+    int64_t plan_grid;     // plan_blocks rounded up to a multiple of 8
+    int64_t static_waves;  // product wavefronts
+};
+
+// One queued item: [0, n_ch) long-row chunks, then medium rows, then the
+// short tiles after the static ones (heaviest kinds first, the smallest
+// items last so that the queues drain evenly).
 template <class S>
-__device__ inline void do_item(const WorkerArgs &a, WaveStage &ws, int lane,
-                               int g, int j, int64_t d, int64_t first,
-                               int64_t n_short_tiles, int64_t n_ch,
-                               int64_t n_long, int passes, const BSrc &src,
+__device__ inline void do_item(const WorkerArgs &a, const ProductShape &ps,
+                               WaveStage &ws, int lane, int g, int j,
+                               int64_t d, int64_t n_ch, int64_t n_med,
+                               int64_t n_long, const BSrc &src,
                                uint32_t row_bytes)
 {
     int64_t row = 0, p0 = 0, p1 = 0;
-    const int64_t n_rest = n_short_tiles - first;
     if (d < n_ch) {
         // The row was cleared (device-coherent stores, completed) before its
         // chunk was published; the atomic adds address it through the
@@ -595,14 +606,17 @@ __device__ inline void do_item(const WorkerArgs &a, WaveStage &ws, int lane,
             do_range<S, true>(a, ws, lane, g, j, row, p0, p1, src, row_bytes);
         else
             note_fault(a, lane);
-    } else if (d < n_ch + n_rest) {
-        do_short_tile<S>(a, ws, lane, g, j, first + (d - n_ch), passes, src, row_bytes);
-    } else {
-        if (wait_for([&]() { return medium_ready(a, d - n_ch - n_rest, &row); }))
+    } else if (d < n_ch + n_med) {
+        if (wait_for([&]() { return medium_ready(a, d - n_ch, &row); }))
             do_range<S, false>(a, ws, lane, g, j, row, a.rowptr[row],
                                a.rowptr[row + 1], src, row_bytes);
         else
             note_fault(a, lane);
+    } else {
+        const int64_t t = d - n_ch - n_med;
+        do_short_tile<S>(a, ws, lane, g, j,
+                         ps.rows_static + t * (int64_t)(ps.dyn_passes * S::R),
+                         ps.dyn_passes, src, row_bytes);
     }
 }
 
@@ -613,13 +627,12 @@ __device__ inline void do_item(const WorkerArgs &a, WaveStage &ws, int lane,
 // logical product wavefront w takes tile w, for w < first), which needs no
 // plan.  Then every wavefront, the planners included, takes the remaining
 // items from kQueues work queues: queue q hands out items q, q + kQueues,
-// ... in the order [long-row chunks | short tiles | medium rows], so every
-// queue holds the same mix, heaviest items first, and a wavefront that
-// started late or drew slow items simply takes fewer.
+// ... in the order [long-row chunks | medium rows | short tiles], so every
+// queue holds the same mix, and a wavefront that started late or drew slow
+// items simply takes fewer.
 template <class S>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4)))
-void call_kernel(WorkerArgs a, int64_t n_short_tiles, int passes,
-                 int64_t plan_blocks, int64_t plan_grid, int64_t static_waves)
+void call_kernel(WorkerArgs a, ProductShape ps)
 {
     __shared__ union {
         WaveStage stage[kWavesPerBlock];
@@ -628,9 +641,9 @@ void call_kernel(WorkerArgs a, int64_t n_short_tiles, int passes,
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = threadIdx.x / kWave;
     const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wid;
-    const bool planner = (int64_t)blockIdx.x < plan_grid;
+    const bool planner = (int64_t)blockIdx.x < ps.plan_grid;
     if (planner) {
-        if ((int64_t)blockIdx.x < plan_blocks) {
+        if ((int64_t)blockIdx.x < ps.plan_blocks) {
             PlanCtx pc;
             pc.rowptr = a.rowptr;
             pc.C = a.C;
@@ -645,9 +658,10 @@ void call_kernel(WorkerArgs a, int64_t n_short_tiles, int passes,
         }
         // Clear the queue counters of the next call on this stream (the
         // previous call, which used them, has ended).
-        if (blockIdx.x == 0 && wid == 0 && lane < kQueues)
-            a.plan.queues[((a.epoch + 1) & 1) * kQueues * kQueueStride +
-                          lane * kQueueStride] = 0;
+        if (blockIdx.x == 0 && wid == 0)
+            for (int q = lane; q < kQueues; q += kWave)
+                a.plan.queues[((a.epoch + 1) & 1) * kQueues * kQueueStride +
+                              q * kQueueStride] = 0;
         __syncthreads();  // the block's LDS now serves the product
     }
 
@@ -662,14 +676,14 @@ void call_kernel(WorkerArgs a, int64_t n_short_tiles, int passes,
             const_cast<void *>(a.B), (short)0,
             (int)(uint32_t)(a.K * a.N * S::ESZ), kBufferWord3);
 
-    const int64_t first = n_short_tiles < static_waves ? n_short_tiles : static_waves;
     if (!planner) {
         // plan_grid is a multiple of 8, so product block b runs on XCD b % 8
-        const int64_t w = xcd_logical_block((int64_t)blockIdx.x - plan_grid,
-                                            (int64_t)gridDim.x - plan_grid) *
+        const int64_t w = xcd_logical_block((int64_t)blockIdx.x - ps.plan_grid,
+                                            (int64_t)gridDim.x - ps.plan_grid) *
                               kWavesPerBlock + wid;
-        if (w < first)
-            do_short_tile<S>(a, ws, lane, g, j, w, passes, src, row_bytes);
+        if (w < ps.first)
+            do_short_tile<S>(a, ws, lane, g, j, w * (int64_t)(ps.passes * S::R),
+                             ps.passes, src, row_bytes);
     }
 
     int64_t n_med = 0, n_long = 0, n_ch = 0;
@@ -677,7 +691,7 @@ void call_kernel(WorkerArgs a, int64_t n_short_tiles, int passes,
         note_fault(a, lane);
         n_med = n_long = n_ch = 0;
     }
-    const int64_t n_dyn = n_ch + (n_short_tiles - first) + n_med;
+    const int64_t n_dyn = n_ch + n_med + ps.n_dyn_tiles;
     const int64_t q = gw % kQueues;
     uint32_t *ctr = a.plan.queues + ((a.epoch & 1) * kQueues + q) * kQueueStride;
     // Lane 0 holds the next grabbed index; it is read (and waited for) only
@@ -691,10 +705,13 @@ void call_kernel(WorkerArgs a, int64_t n_short_tiles, int passes,
             break;
         if (lane == 0)
             next = atomicAdd(ctr, 1u);
-        do_item<S>(a, ws, lane, g, j, d, first, n_short_tiles, n_ch, n_long,
-                   passes, src, row_bytes);
+        do_item<S>(a, ps, ws, lane, g, j, d, n_ch, n_med, n_long, src, row_bytes);
     }
 }
+
+// Short tiles handed out by the queues hold 1/kDynTileDiv of the rows of
+// the static ones (at least R rows), so the queues end on small items.
+constexpr int kDynTileDiv = 2;
 
 template <class S>
 hipError_t launch_shape(const WorkerArgs &a, hipStream_t stream,
@@ -713,15 +730,16 @@ hipError_t launch_shape(const WorkerArgs &a, hipStream_t stream,
             return err;
         resident_blocks = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
     }
+    ProductShape ps;
     // Plan workgroups first (padded to a multiple of the 8 XCDs), product
     // workgroups in the remaining slots, so that every workgroup starts at
     // once.
-    const int64_t plan_blocks = (a.shape.n_tiles + kPlanBlockWaves - 1) / kPlanBlockWaves;
-    const int64_t plan_grid = (plan_blocks + 7) / 8 * 8;
-    int64_t product_blocks = resident_blocks - plan_grid;
+    ps.plan_blocks = (a.shape.n_tiles + kPlanBlockWaves - 1) / kPlanBlockWaves;
+    ps.plan_grid = (ps.plan_blocks + 7) / 8 * 8;
+    int64_t product_blocks = resident_blocks - ps.plan_grid;
     if (product_blocks < 8)
         product_blocks = 8;
-    const int64_t product_waves = product_blocks * kWavesPerBlock;
+    ps.static_waves = product_blocks * kWavesPerBlock;
     // Short tiles: P rows per group (T = P*R rows, at most 64), at most 8,
     // small enough that the staged entries fit (T * short_max <= kShortCap),
     // and fewer when M is too small to give every product wavefront a tile.
@@ -731,14 +749,18 @@ hipError_t launch_shape(const WorkerArgs &a, hipStream_t stream,
         max_passes = kShortCap / (S::R * smax);
     if (max_passes < 1)
         return hipErrorInvalidValue;  // short_max above the group capacity
-    int64_t passes = a.M / ((int64_t)S::R * product_waves);
+    int64_t passes = a.M / ((int64_t)S::R * ps.static_waves);
     passes = passes < 1 ? 1 : (passes > max_passes ? max_passes : passes);
-    const int64_t tile = passes * S::R;
-    const int64_t n_short_tiles = (a.M + tile - 1) / tile;
-    const int64_t blocks = plan_grid + product_blocks;
+    ps.passes = (int)passes;
+    ps.dyn_passes = (int)(passes / kDynTileDiv > 1 ? passes / kDynTileDiv : 1);
+    const int64_t ts = passes * S::R, td = (int64_t)ps.dyn_passes * S::R;
+    const int64_t n_static = (a.M + ts - 1) / ts;
+    ps.first = n_static < ps.static_waves ? n_static : ps.static_waves;
+    ps.rows_static = ps.first * ts < a.M ? ps.first * ts : a.M;
+    ps.n_dyn_tiles = (a.M - ps.rows_static + td - 1) / td;
+    const int64_t blocks = ps.plan_grid + product_blocks;
     hipExtLaunchKernelGGL(call_kernel<S>, dim3((unsigned)blocks), dim3(kBlock),
-                          0, stream, start, stop, 0, a, n_short_tiles, (int)passes,
-                          plan_blocks, plan_grid, product_waves);
+                          0, stream, start, stop, 0, a, ps);
     return hipGetLastError();
 }
 
