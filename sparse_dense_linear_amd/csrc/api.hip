@@ -56,11 +56,15 @@ spmm_status_t resolve(int32_t dtype, int64_t N, const spmm_tuning_t *req,
     const WorkerConfig cfg = choose_worker(dtype, N > 0 ? N : 1, nullptr, nullptr);
     const int R = kWave / cfg.group;
     const int U = unroll_of(cfg.nv);
-    // Defaults: a short row fits two unrolled gather rounds of one group;
-    // a wavefront item (medium row or long-row chunk) is about eight rounds
-    // of all R groups, kept within [256, 4096] entries.
-    int64_t chunk = (int64_t)R * U * 8;
-    chunk = chunk < 256 ? 256 : (chunk > 4096 ? 4096 : chunk);
+    // Defaults: a short row fits two unrolled gather rounds of one group; a
+    // wavefront item (medium row or long-row chunk) holds 1024 / R entries
+    // (kept within [128, 4096]), so each of its R groups gathers about 1024
+    // / R^2 rows of B: wide rows of B (few groups) get long items, narrow
+    // rows short ones, which keeps an item's chain of dependent gathers
+    // short where many items run side by side.  Measured on the power-law
+    // (R = 4) and the pruned and skewed (R = 1) workloads.
+    int64_t chunk = 1024 / R;
+    chunk = chunk < 128 ? 128 : (chunk > 4096 ? 4096 : chunk);
     spmm_tuning_t t;
     t.short_max = 2 * U;
     t.chunk_nnz = (int32_t)chunk;

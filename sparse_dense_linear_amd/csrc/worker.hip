@@ -150,6 +150,8 @@ struct Entry {
 // Per-wavefront LDS staging area.  A short tile stages at most kShortCap
 // entries (the host sizes tiles so that T * short_max <= kShortCap); medium
 // rows and long chunks use the first 64 entries.
+constexpr int kStageSlots = kShortCap / kWave;  // staged entries per lane
+
 struct WaveStage {
     Entry ent[kShortCap];
     uint8_t rid[kShortCap];   // row of the entry within its tile
@@ -470,22 +472,37 @@ __device__ void do_short_tile(const WorkerArgs &a, WaveStage &ws, int lane,
     // lanes' offsets, so each round is one coalesced load per lane however
     // the entries are spread over rows.
     const int total = __shfl(off + slen, kWave - 1);
-    for (int e0 = 0; e0 < total; e0 += kWave) {
-        const int e = e0 + lane < total ? e0 + lane : total - 1;
-        int l = 0;
+    // All loads first (slot i holds entry i*64 + lane), then the LDS
+    // stores, so the whole tile is staged in one memory round trip.
+    int scol[kStageSlots];
+    float sval[kStageSlots];
+    int srow[kStageSlots];
 #pragma unroll
-        for (int step = kWave / 2; step > 0; step >>= 1) {
-            const int cand = l + step;
-            if (__shfl(off, cand) <= e)
-                l = cand;
+    for (int i = 0; i < kStageSlots; ++i) {
+        if (i * kWave < total) {  // wave-uniform
+            const int e = i * kWave + lane < total ? i * kWave + lane : total - 1;
+            int l = 0;
+#pragma unroll
+            for (int step = kWave / 2; step > 0; step >>= 1) {
+                const int cand = l + step;
+                if (__shfl(off, cand) <= e)
+                    l = cand;
+            }
+            const int64_t p = (int64_t)__shfl(s, l) + (e - __shfl(off, l));
+            scol[i] = a.colind[p];
+            sval[i] = load_val<S::DT>(a.vals, p);
+            srow[i] = l;
         }
-        const int64_t p = (int64_t)__shfl(s, l) + (e - __shfl(off, l));
-        Entry en;
-        en.col = a.colind[p];
-        en.val = load_val<S::DT>(a.vals, p);
-        if (e0 + lane < total) {
+    }
+#pragma unroll
+    for (int i = 0; i < kStageSlots; ++i) {
+        const int e = i * kWave + lane;
+        if (i * kWave < total && e < total) {
+            Entry en;
+            en.col = scol[i];
+            en.val = sval[i];
             ws.ent[e] = en;
-            ws.rid[e] = (uint8_t)l;
+            ws.rid[e] = (uint8_t)srow[i];
         }
     }
 
@@ -627,7 +644,7 @@ __device__ inline void do_item(const WorkerArgs &a, const ProductShape &ps,
 // logical product wavefront w takes tile w, for w < first), which needs no
 // plan.  Then every wavefront, the planners included, takes the remaining
 // items from kQueues work queues: queue q hands out items q, q + kQueues,
-// ... in the order [long-row chunks | medium rows | short tiles], so every
+// ... of the list [long-row chunks | medium rows | short tiles], so every
 // queue holds the same mix, and a wavefront that started late or drew slow
 // items simply takes fewer.
 template <class S>
@@ -692,6 +709,10 @@ void call_kernel(WorkerArgs a, ProductShape ps)
         n_med = n_long = n_ch = 0;
     }
     const int64_t n_dyn = n_ch + n_med + ps.n_dyn_tiles;
+    // One item per grab: consecutive items go to different wavefronts at
+    // about the same time, so the whole GPU sweeps the item list in order
+    // (rows that share columns of B, as in banded matrices, are gathered
+    // together).  Grabs are device atomics on kQueues counters.
     const int64_t q = gw % kQueues;
     uint32_t *ctr = a.plan.queues + ((a.epoch & 1) * kQueues + q) * kQueueStride;
     // Lane 0 holds the next grabbed index; it is read (and waited for) only

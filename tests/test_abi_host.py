@@ -50,7 +50,8 @@ def test_status_strings():
 def test_resolve_defaults_are_consistent(dtype, N):
     t = sdl.resolve_tuning(dtype, N)
     assert 0 <= t.short_max <= t.medium_max
-    assert 256 <= t.chunk_nnz <= 4096
+    assert 128 <= t.chunk_nnz <= 4096
+    assert t.medium_max == t.chunk_nnz
     # explicit values win over defaults
     u = sdl.resolve_tuning(dtype, N, sdl.Tuning(3, 77, 11))
     assert (u.short_max, u.medium_max, u.chunk_nnz) == (3, 77, 11)
