@@ -97,6 +97,59 @@ def cpu_baseline(p, budget_s: float = 10.0) -> dict:
                       f"{reps} repetitions in {el:.1f} s"}
 
 
+def gather_ceiling(torch, dev) -> dict:
+    """Bandwidth of the bare access pattern: output row i = sum of D random
+    rows of B (D gathers of N fp32 + one row store per output row), for a B
+    the size of the power-law workload's (67 MB, fits the Infinity Cache)
+    and one 16x larger (1 GiB, does not), and of a 1 GiB device copy.
+    Bytes counted: gathers + index reads + C writes (copy: read + write)."""
+    import ctypes
+    from sparse_dense_linear_amd import build as B_
+    lib = ctypes.CDLL(B_.CEILING_PATH)
+    lib.sdl_gather_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.c_void_p]
+    lib.sdl_gather_ceiling.restype = ctypes.c_int
+    stream = torch.cuda.current_stream(dev)
+    N, M, reps = 64, 262144, 20
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    out = {"kernel": "gather_rows (ceiling.hip)", "N": N, "M": M, "reps": reps,
+           "runs": []}
+    for K in (262144, 4194304):
+        Bm = torch.randn(K * N, dtype=torch.float32, device=dev)
+        for D in (1, 2, 4, 8):
+            idx = torch.randint(0, K, (M * D,), dtype=torch.int32, device=dev)
+            C = torch.empty(M * N, dtype=torch.float32, device=dev)
+
+            def run():
+                rc = lib.sdl_gather_ceiling(Bm.data_ptr(), idx.data_ptr(), C.data_ptr(),
+                                            M, N, D, stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"sdl_gather_ceiling returned {rc}")
+            t = timed(run)
+            nbytes = M * D * N * 4 + M * D * 4 + M * N * 4
+            out["runs"].append({"B_bytes": K * N * 4, "D": D, "us": round(t * 1e6, 2),
+                                "GBps": round(nbytes / t / 1e9, 1)})
+        del Bm
+    a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    t = timed(lambda: b.copy_(a))
+    out["copy_1GiB_GBps"] = round(2 * a.numel() * 4 / t / 1e9, 1)
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +161,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for counter scaling)")
+    ap.add_argument("--gather-ceiling", action="store_true",
+                    help="only time the bare row-gather kernel and a device copy")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -133,6 +188,10 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n,
                           "launches": 5}))
+        return 0
+
+    if args.gather_ceiling:
+        print(json.dumps(gather_ceiling(torch, dev)), flush=True)
         return 0
 
     p = W.make(args.workload)

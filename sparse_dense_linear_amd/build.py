@@ -1,7 +1,9 @@
-"""Compile the HIP sources of this package into ``libsdl_spmm.so`` (gfx950).
+"""Compile the HIP sources of this package (gfx950).
 
-Each translation unit is compiled to an object under ``_build/`` (in
-parallel), then linked into a shared library placed next to this file.
+``libsdl_spmm.so`` is the library: each of its translation units is
+compiled to an object under ``_build/`` (in parallel) and linked next to
+this file.  ``libsdl_ceiling.so`` holds the measurement kernel that
+``bench.py --gather-ceiling`` times (not part of the product path).
 Packed fp32 instructions are disabled for all device code.
 """
 from __future__ import annotations
@@ -19,6 +21,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libsdl_spmm.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["api.hip", "plan.hip", "worker.hip"]
+CEILING_SOURCE = "ceiling.hip"
+CEILING_PATH = os.path.join(HERE, "libsdl_ceiling.so")
 ARCH = "gfx950"
 
 
@@ -54,14 +58,15 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")
         return obj
 
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(one, SOURCES))
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        objs = list(ex.map(one, SOURCES + [CEILING_SOURCE]))
+    for target, parts in ((LIB_PATH, objs[:-1]), (CEILING_PATH, objs[-1:])):
+        tmp = target + ".tmp"
+        cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *parts]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"link failed:\n{res.stderr}")
+        os.replace(tmp, target)
     return LIB_PATH
 
 

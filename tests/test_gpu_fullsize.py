@@ -22,6 +22,7 @@ def log(msg):
 
 
 @pytest.mark.parametrize("name", ["uniform_1k_n32", "powerlaw_262k_n64",
+                                  "powerlaw_262k_n64_mean16",
                                   "pruned_4k_n256_bf16", "pruned_4k_n256_f32"])
 def test_full_compare(name):
     t = time.time()

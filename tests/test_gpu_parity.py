@@ -25,7 +25,8 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 # Row lengths around every routing boundary of the default thresholds, and
 # long rows spanning many chunks; K must exceed the longest row.
 EDGE_LENGTHS = [0, 1, 2, 3, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65,
-                127, 128, 129, 255, 256, 257, 511, 512, 513, 1000, 2049, 5000]
+                127, 128, 129, 255, 256, 257, 511, 512, 513, 1000, 1023, 1024,
+                1025, 2047, 2048, 2049, 5000]
 
 
 def edge_problem(N, dtype, M=300, K=6000, seed=0):
@@ -188,6 +189,72 @@ def test_nonneg_equals_bound():
     C = run_gpu(p)
     _, Sref = reference(p)
     assert np.all(np.abs(C - Sref) <= 1e-5 * Sref + 1e-6)
+
+
+def _with_vals(p, vals):
+    return W.CsrProblem(p.name, p.M, p.K, p.N, p.rowptr, p.colind,
+                        np.ascontiguousarray(vals), p.B, p.dtype)
+
+
+def _single_wave_rows(p):
+    """Rows computed by one wavefront (not split into chunks): their results
+    do not depend on the order of atomic adds."""
+    t = sdl.resolve_tuning(0 if p.dtype == "f32" else 1, p.N)
+    return np.diff(p.rowptr.astype(np.int64)) <= t.medium_max
+
+
+@pytest.mark.parametrize("N", [4, 64, 256])
+def test_row_locality_bitwise(N):
+    """Changing the values of some rows leaves every other row bit for bit
+    unchanged (rows are independent; no state leaks between work items)."""
+    p = edge_problem(N, "f32", M=400, seed=6)
+    C1 = run_gpu(p)
+    rng = np.random.default_rng(1)
+    changed = rng.random(p.M) < 0.3
+    mask = np.repeat(changed, np.diff(p.rowptr.astype(np.int64)))
+    v2 = p.vals.copy()
+    v2[mask] = rng.uniform(-1, 1, mask.sum()).astype(np.float32)
+    C2 = run_gpu(_with_vals(p, v2))
+    keep = ~changed & _single_wave_rows(p)
+    assert keep.sum() > 100
+    assert np.array_equal(C1[keep], C2[keep])
+    Cref, Sref = reference(_with_vals(p, v2))
+    assert_parity(C2, Cref, Sref, "f32", "changed rows")
+
+
+def test_additivity():
+    """C(v1 + v2) = C(v1) + C(v2) within the sum of the bounds."""
+    p = edge_problem(64, "f32", M=300, seed=7)
+    rng = np.random.default_rng(2)
+    v1 = p.vals
+    v2 = rng.uniform(-1, 1, p.vals.shape[0]).astype(np.float32)
+    v12 = (v1.astype(np.float64) + v2).astype(np.float32)
+    C1, C2, C12 = (run_gpu(_with_vals(p, v)) for v in (v1, v2, v12))
+    _, S1 = reference(_with_vals(p, v1))
+    _, S2 = reference(_with_vals(p, v2))
+    _, S12 = reference(_with_vals(p, v12))
+    err = np.abs(C12.astype(np.float64) - C1 - C2)
+    # rounding v1 + v2 to fp32 moves each product by at most 2^-24 of it
+    lim = 1e-5 * (S1 + S2 + S12) + 2.0 ** -24 * S12 + 3e-6
+    assert np.all(err <= lim)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_permuted_entries_within_bound(dtype):
+    """Shuffling the stored entries inside each row (unsorted colind) gives
+    the same product within the bound."""
+    p = edge_problem(64, dtype, M=300, seed=8)
+    rng = np.random.default_rng(3)
+    rp = p.rowptr.astype(np.int64)
+    perm = np.arange(p.nnz)
+    for i in range(p.M):
+        seg = perm[rp[i]:rp[i + 1]]
+        rng.shuffle(seg)
+    q = W.CsrProblem(p.name, p.M, p.K, p.N, p.rowptr,
+                     np.ascontiguousarray(p.colind[perm]),
+                     np.ascontiguousarray(p.vals[perm]), p.B, p.dtype)
+    Cref, Sref = reference(p)
+    assert_parity(run_gpu(q), Cref, Sref, dtype, "permuted")
 
 
 # ------------------------------------------------------------------ plan

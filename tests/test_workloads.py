@@ -109,7 +109,16 @@ def test_bf16_rounding_matches_torch():
 
 def test_registry_names():
     assert set(W.WORKLOADS) == {"uniform_1k_n32", "powerlaw_262k_n64",
+                                "powerlaw_262k_n64_mean16",
                                 "pruned_4k_n256_bf16", "pruned_4k_n256_f32",
                                 "banded_4m_n128", "skew_1m_n512_bf16"}
     p = W.make("uniform_1k_n32")
     assert (p.M, p.K, p.N, p.nnz) == (1024, 1024, 32, 16384)
+
+
+def test_powerlaw_mean16_exponent():
+    """The secondary power-law case: exponent 1.7694 on {1..8192} has mean
+    row length 16 (the law's mean, computed exactly)."""
+    d = np.arange(1, 8193, dtype=np.float64)
+    w = d ** -1.7694
+    assert abs((d * w).sum() / w.sum() - 16.0) < 0.01

@@ -313,6 +313,10 @@ def skew_rows(M=1048576, K=None, N=512, hub_frac=0.001, hub_lo=20000,
 WORKLOADS = {
     "uniform_1k_n32": lambda: uniform_rows(),
     "powerlaw_262k_n64": lambda: powerlaw_rows(),
+    # secondary power-law case: the exponent that gives mean row length 16
+    # on {1..8192}
+    "powerlaw_262k_n64_mean16": lambda: powerlaw_rows(
+        alpha=1.7694, seed=22, name="powerlaw_262k_n64_mean16"),
     "pruned_4k_n256_bf16": lambda: bernoulli_rows(dtype="bf16"),
     "pruned_4k_n256_f32": lambda: bernoulli_rows(dtype="f32"),
     "banded_4m_n128": lambda: banded_rows(),
