@@ -13,6 +13,12 @@ Pages cited:
 Contents
   spmm_ref   -- C = A*B and the bound S = |A|*|B| in fp64 ([IntelMax], SpMM
                 operation, Fig. 5 / Algorithm 2), computed by ``spmm_ref.c``.
+  sddmm_ref  -- the SDDMM values A[p] = <C_i, B_j> on a CSR pattern and their
+                bound ([IntelMax], SDDMM operation, Fig. 3 / Algorithm 1),
+                computed by ``sddmm_ref.c``.
+  fusedmm_ref -- E_i = sum_p <C_i, B_j> D_j over the pattern and its bound
+                ([IntelMax], FusedMM operation, Fig. 6 / Algorithm 3),
+                computed by ``sddmm_ref.c``.
   plan_ref   -- the row-binning plan: which rows are short, medium or long, and
                 how long rows are cut into nnz chunks (see its docstring).
   widen_bf16 -- exact bf16 -> float64 widening used by the oracle.
@@ -36,23 +42,32 @@ _LIB_PATH = os.path.join(_HERE, "liboracle_spmm.so")
 F32 = 0
 BF16 = 1
 
+_SDDMM_SRC = os.path.join(_HERE, "sddmm_ref.c")
+_SDDMM_LIB_PATH = os.path.join(_HERE, "liboracle_sddmm.so")
+
 _lib = None
+_sddmm_lib = None
+
+
+def compile_oracle(src: str, out: str) -> str:
+    """gcc a C oracle source into a shared library (-ffp-contract=off keeps
+    every a*b + acc a separate multiply and add, so the fp64 results are
+    reproducible)."""
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+           "-ffp-contract=off", "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
 
 
 def build(force: bool = True) -> str:
-    """Compile ``spmm_ref.c`` with gcc into ``liboracle_spmm.so``.
-
-    -ffp-contract=off keeps every a*b + acc a separate multiply and add, so
-    the fp64 results are reproducible.
-    """
-    if not force and os.path.exists(_LIB_PATH) and \
-            os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
-        return _LIB_PATH
-    tmp = _LIB_PATH + ".tmp"
-    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
-           "-ffp-contract=off", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB_PATH)
+    """Compile ``spmm_ref.c`` into ``liboracle_spmm.so`` and ``sddmm_ref.c``
+    into ``liboracle_sddmm.so``; returns the first path."""
+    for src, out in ((_SRC, _LIB_PATH), (_SDDMM_SRC, _SDDMM_LIB_PATH)):
+        if force or not os.path.exists(out) or \
+                os.path.getmtime(out) < os.path.getmtime(src):
+            compile_oracle(src, out)
     return _LIB_PATH
 
 
@@ -74,12 +89,119 @@ def load_library(path: str):
     return lib
 
 
+def load_sddmm_library(path: str):
+    """Load an oracle shared library built from ``sddmm_ref.c``."""
+    lib = ctypes.CDLL(path)
+    lib.oracle_sddmm.restype = ctypes.c_int
+    lib.oracle_sddmm.argtypes = [
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p,
+    ]
+    lib.oracle_fusedmm.restype = ctypes.c_int
+    lib.oracle_fusedmm.argtypes = [
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+    ]
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
         build(force=False)
         _lib = load_library(_LIB_PATH)
     return _lib
+
+
+def _load_sddmm():
+    global _sddmm_lib
+    if _sddmm_lib is None:
+        build(force=False)
+        _sddmm_lib = load_sddmm_library(_SDDMM_LIB_PATH)
+    return _sddmm_lib
+
+
+def _same_kind(*arrays) -> int:
+    kinds = {_kind_of(a) for a in arrays}
+    if len(kinds) != 1:
+        raise TypeError("dense operands must all be float32 or all bf16 bits")
+    return kinds.pop()
+
+
+def sddmm_ref(rowptr, colind, C, B, N: int, rows=None, library=None):
+    """fp64 oracle for SDDMM on a CSR pattern.
+
+    [IntelMax], SDDMM operation (Fig. 3, Algorithm 1): the entry p of row i
+    at column j = colind[p] gets the dot product of row C_i (C is M x N)
+    with row B_j (B is K x N; column j of B^T).
+
+    Returns (A, S): float64 arrays with one value per stored entry -- all
+    entries in CSR order (index p - rowptr[0]) when ``rows`` is None, else
+    the entries of the listed rows packed in list order -- and the bound
+    S[p] = sum_n |C[i,n]| |B[j,n]|.
+    """
+    lib = _load_sddmm() if library is None else library
+    rowptr = np.ascontiguousarray(rowptr, dtype=np.int32)
+    colind = np.ascontiguousarray(colind, dtype=np.int32)
+    C = np.ascontiguousarray(C)
+    B = np.ascontiguousarray(B)
+    M = rowptr.shape[0] - 1
+    if rows is None:
+        rows_arr, count, off = None, M, None
+        total = int(rowptr[-1]) - int(rowptr[0]) if M >= 0 else 0
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        count = rows_arr.shape[0]
+        off = np.empty(count, dtype=np.int64)
+        lens = rowptr[1:].astype(np.int64) - rowptr[:-1]
+        total = int(lens[rows_arr].sum()) if count else 0
+    A = np.empty(total, dtype=np.float64)
+    S = np.empty(total, dtype=np.float64)
+    rc = lib.oracle_sddmm(M, N, rowptr.ctypes.data, colind.ctypes.data,
+                          _same_kind(C, B), C.ctypes.data, B.ctypes.data,
+                          None if rows_arr is None else rows_arr.ctypes.data,
+                          count, None if off is None else off.ctypes.data,
+                          A.ctypes.data, S.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_sddmm rejected its arguments")
+    return A, S
+
+
+def fusedmm_ref(rowptr, colind, C, B, D, N: int, rows=None, library=None):
+    """fp64 oracle for FusedMM on a CSR pattern.
+
+    [IntelMax], FusedMM operation (Fig. 6, Algorithm 3): for each stored
+    entry of row i (column j) in CSR order, its SDDMM value a = <C_i, B_j>
+    is computed and a * D_j is added into E_i (D is K x N).
+
+    Returns (E, T): float64 arrays of shape (len(rows) or M, N), and the
+    bound T[i,n] = sum_p S[p] |D[j,n]| with S[p] the SDDMM bound.
+    """
+    lib = _load_sddmm() if library is None else library
+    rowptr = np.ascontiguousarray(rowptr, dtype=np.int32)
+    colind = np.ascontiguousarray(colind, dtype=np.int32)
+    C = np.ascontiguousarray(C)
+    B = np.ascontiguousarray(B)
+    D = np.ascontiguousarray(D)
+    M = rowptr.shape[0] - 1
+    if rows is None:
+        rows_arr, count = None, M
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        count = rows_arr.shape[0]
+    E = np.empty((count, N), dtype=np.float64)
+    T = np.empty((count, N), dtype=np.float64)
+    rc = lib.oracle_fusedmm(M, N, rowptr.ctypes.data, colind.ctypes.data,
+                            _same_kind(C, B, D), C.ctypes.data, B.ctypes.data,
+                            D.ctypes.data,
+                            None if rows_arr is None else rows_arr.ctypes.data,
+                            count, E.ctypes.data, T.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_fusedmm rejected its arguments")
+    return E, T
 
 
 def num_threads() -> int:
