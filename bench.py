@@ -41,6 +41,7 @@ METRIC = ("SpMM GFLOP/s (2·nnz·N) and effective HBM GB/s as % of peak, "
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "powerlaw_262k_n64"
 KERNEL_SOURCES = ["sparse_dense_linear_amd/csrc/worker.hip",
+                  "sparse_dense_linear_amd/csrc/sddmm.hip",
                   "sparse_dense_linear_amd/csrc/plan_device.h",
                   "sparse_dense_linear_amd/csrc/plan.hip",
                   "sparse_dense_linear_amd/csrc/internal.h",
@@ -63,14 +64,20 @@ def min_bytes(p) -> int:
     return 4 * (p.M + 1) + p.nnz * (4 + s_val) + p.K * p.N * s_b + 4 * p.M * p.N
 
 
+def sddmm_min_bytes(p) -> int:
+    """rowptr + colind (nnz) + C (M x N) and B (K x N) once + A written."""
+    s_d = p.B.dtype.itemsize
+    return 4 * (p.M + 1) + 4 * p.nnz + (p.M + p.K) * p.N * s_d + 4 * p.nnz
+
+
 def flops(p) -> int:
     return 2 * p.nnz * p.N
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per worker launch from the committed counter summary, if it
-    was taken on the current kernel sources."""
-    path = COUNTER_FILE.format(workload=workload)
+def measured_traffic(workload: str, op: str = "spmm"):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources."""
+    path = COUNTER_FILE.format(workload=workload if op == "spmm" else f"{op}_{workload}")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -81,19 +88,22 @@ def measured_traffic(workload: str):
     return float(m_b.group(1))
 
 
-def cpu_baseline(p, budget_s: float = 10.0) -> dict:
+def cpu_baseline(p, budget_s: float = 10.0, op: str = "spmm", dense=None) -> dict:
     import oracle
     reps = 0
     t0 = time.perf_counter()
     while True:
-        oracle.spmm_ref(p.rowptr, p.colind, p.vals, p.B, p.N, with_bound=False)
+        if op == "spmm":
+            oracle.spmm_ref(p.rowptr, p.colind, p.vals, p.B, p.N, with_bound=False)
+        else:
+            oracle.sddmm_ref(p.rowptr, p.colind, dense, p.B, p.N)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 1000:
             break
     return {"value": round(flops(p) * reps / el / 1e9, 4), "unit": "GFLOP/s",
             "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"the whole {p.name} matrix (C only, no bound), "
+            "sample": f"the whole {p.name} matrix ({'C only, no bound' if op == 'spmm' else 'SDDMM values and bound'}), "
                       f"{reps} repetitions in {el:.1f} s"}
 
 
@@ -163,6 +173,9 @@ def main() -> int:
                     help="only run a 1 GiB device copy (for counter scaling)")
     ap.add_argument("--gather-ceiling", action="store_true",
                     help="only time the bare row-gather kernel and a device copy")
+    ap.add_argument("--op", default="spmm", choices=["spmm", "sddmm"],
+                    help="spmm: C = A*B (the headline); sddmm: A = (C B^T) sampled "
+                         "on the workload's pattern, C drawn like B")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -205,12 +218,25 @@ def main() -> int:
         vals = torch.from_numpy(p.vals.view(np.int16)).to(dev)
         B = torch.from_numpy(p.B.reshape(-1).view(np.int16)).to(dev)
         fn = sdl.spmm_csr_bf16in_f32acc
-    C = torch.empty(p.M * p.N, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    if args.op == "spmm":
+        C = torch.empty(p.M * p.N, dtype=torch.float32, device=dev)
 
-    def step():
-        fn(rowptr, colind, vals, B, C, p.M, p.K, p.N, stream)
+        def step():
+            fn(rowptr, colind, vals, B, C, p.M, p.K, p.N, stream)
+        op_flops, op_bytes = flops(p), min_bytes(p)
+    else:
+        # dense left operand: M x N, same element type and recipe as B
+        Cd = torch.randn(p.M * p.N, dtype=torch.float32, device=dev,
+                         generator=torch.Generator(device=dev).manual_seed(7))
+        if p.dtype != "f32":
+            Cd = Cd.to(torch.bfloat16).view(torch.int16)
+        A = torch.empty(p.nnz, dtype=torch.float32, device=dev)
+        sfn = sdl.sddmm_csr_f32 if p.dtype == "f32" else sdl.sddmm_csr_bf16in_f32acc
 
+        def step():
+            sfn(rowptr, colind, Cd, B, A, p.M, p.K, p.N, stream)
+        op_flops, op_bytes = flops(p), sddmm_min_bytes(p)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -237,8 +263,8 @@ def main() -> int:
         raise RuntimeError(f"{faults} items were left undone (plan entries never visible)")
 
     ms_per_step = elapsed * 1e3 / args.steps
-    gflops = flops(p) / (ms_per_step * 1e-3) / 1e9
-    mb = min_bytes(p)
+    gflops = op_flops / (ms_per_step * 1e-3) / 1e9
+    mb = op_bytes
     eff = mb / (ms_per_step * 1e-3) / 1e9
     worker_avg_ms = worker_ms / max(ncalls, 1)
     achieved = mb / (worker_avg_ms * 1e-3) / 1e9 if worker_avg_ms > 0 else None
@@ -259,7 +285,7 @@ def main() -> int:
     cold_med = float(np.median(cold)) if cold else None
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.op == "spmm" else METRIC.replace("SpMM", "SDDMM"),
         "value": round(gflops, 3),
         "unit": "GFLOP/s",
         "n_gpus": 1,
@@ -271,13 +297,13 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32" if p.dtype == "f32" else "bf16-in/f32-acc",
         "data": "synthetic",
-        "config": {"workload": p.name, "M": p.M, "K": p.K, "N": p.N,
+        "config": {"workload": p.name, "op": args.op, "M": p.M, "K": p.K, "N": p.N,
                    "nnz": p.nnz, **{k: v for k, v in p.meta.items()
                                     if k not in ("hubs",)}},
         "eff_GBps": round(eff, 2),
         "hbm_frac": round(eff / HBM_PEAK_GBPS, 4),
         "min_bytes": mb,
-        "flops_per_step": flops(p),
+        "flops_per_step": op_flops,
         "kernel_ms": {"call": round(worker_avg_ms, 6)},
         "roofline": {
             "bound": "hbm",
@@ -285,16 +311,20 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": None if achieved is None else round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(p.name),
+            "traffic": measured_traffic(p.name, args.op),
         },
         "cold": {"median_ms": cold_med, "best_ms": min(cold) if cold else None,
                  "reps": len(cold),
                  "eff_GBps_median": None if not cold_med else round(mb / (cold_med * 1e-3) / 1e9, 2),
-                 "gflops_median": None if not cold_med else round(flops(p) / (cold_med * 1e-3) / 1e9, 3)},
+                 "gflops_median": None if not cold_med else round(op_flops / (cold_med * 1e-3) / 1e9, 3)},
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+        dense = None
+        if args.op == "sddmm":
+            dense = Cd.cpu().numpy()
+            dense = dense.view(np.uint16) if p.dtype != "f32" else dense
+        out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds, args.op, dense)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -167,6 +167,40 @@ spmm_status_t spmm_timing_read(double *plan_ms, double *worker_ms,
                                int64_t *calls);
 
 /*
+ * Sampled dense-dense product (SDDMM) on the pattern of a CSR matrix.
+ * [IntelMax] "Performance Optimization of Deep Learning Sparse Matrix
+ * Kernels on Intel Max Series GPU", the SDDMM operation (Fig. 3, Algorithm
+ * 1): the stored entry p of row i, at column j = colind[p], gets the dot
+ * product of row i of C with column j of B^T (row j of B):
+ *
+ *     A[p - rowptr[0]] = sum over n < N of C[i*N + n] * B[j*N + n]
+ *
+ *   rowptr  int32[M+1]  as for the product (absolute offsets; a view works)
+ *   colind  int32[nnz]  0 <= colind[p] < K
+ *   C       M x N       row-major, float32 (or bf16 bits for the bf16 entry)
+ *   B       K x N       row-major, same element type as C
+ *   A       float32[nnz] output, one value per stored entry in CSR order;
+ *                       it is overwritten (not scaled by earlier values)
+ *   nnz     rowptr[M] - rowptr[0], the length of A (a precondition, as are
+ *           the other CSR invariants)
+ *
+ * Ownership, asynchrony and errors as for the product.  nnz == 0 returns
+ * at once; N == 0 with stored entries is UNSUPPORTED.  Numerics: products
+ * and sums in fp32 with fused multiply-adds, in an order that differs from
+ * the sequential one; bf16 operands are widened exactly.  Every value is
+ * computed by one wavefront, so results repeat bit for bit.
+ */
+spmm_status_t sddmm_csr_f32(const int32_t *rowptr, const int32_t *colind,
+                            const float *C, const float *B, float *A,
+                            int64_t M, int64_t K, int64_t N, int64_t nnz,
+                            void *stream);
+spmm_status_t sddmm_csr_bf16in_f32acc(const int32_t *rowptr,
+                                      const int32_t *colind, const uint16_t *C,
+                                      const uint16_t *B, float *A, int64_t M,
+                                      int64_t K, int64_t N, int64_t nnz,
+                                      void *stream);
+
+/*
  * Health check for tests.  Inside a call, product wavefronts poll for the
  * plan entries they need while the plan workgroups of the same launch write
  * them; each poll is bounded (about a second), and an item whose entry

@@ -18,6 +18,9 @@ from ._binding import (  # noqa: F401
     lib_path,
     plan_export,
     resolve_tuning,
+    sddmm,
+    sddmm_csr_bf16in_f32acc,
+    sddmm_csr_f32,
     spmm,
     spmm_csr_bf16in_f32acc,
     spmm_csr_f32,

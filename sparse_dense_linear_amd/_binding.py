@@ -77,6 +77,10 @@ def lib() -> ctypes.CDLL:
                                    ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_int64)]
     L.spmm_stream_faults.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]
+    L.sddmm_csr_f32.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
+    L.sddmm_csr_bf16in_f32acc.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
+    for name in ("sddmm_csr_f32", "sddmm_csr_bf16in_f32acc"):
+        getattr(L, name).restype = I32
     for name in ("spmm_csr_f32", "spmm_csr_bf16in_f32acc", "spmm_csr_tuned",
                  "spmm_resolve_tuning", "spmm_plan_export", "spmm_timing_enable",
                  "spmm_timing_read", "spmm_stream_faults"):
@@ -192,6 +196,69 @@ def spmm(rowptr, colind, vals, B, M: int | None = None, stream=None):
     else:
         spmm_csr_bf16in_f32acc(rowptr, colind, vals, B, C, M, K, N, stream)
     return C
+
+
+def _check_sddmm(rowptr, colind, C, B, A, M, K, N, dtypes):
+    torch = _torch()
+    dev = A.device
+    for name, t in {"rowptr": rowptr, "colind": colind, "C": C, "B": B, "A": A}.items():
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device != dev or dev.type != "cuda":
+            raise ValueError(f"{name} must live on the same GPU as A")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if rowptr.dtype != torch.int32 or colind.dtype != torch.int32:
+        raise TypeError("rowptr and colind must be int32")
+    if C.dtype not in dtypes or B.dtype not in dtypes:
+        raise TypeError(f"C and B must be one of {dtypes}")
+    if A.dtype != torch.float32:
+        raise TypeError("A must be float32")
+    if rowptr.numel() != M + 1:
+        raise ValueError("rowptr must hold M+1 entries")
+    if C.numel() != M * N or B.numel() != K * N:
+        raise ValueError("C must hold M*N and B K*N elements")
+    if A.numel() > colind.numel():
+        raise ValueError("A holds one value per stored entry: at most len(colind)")
+    return dev
+
+
+def sddmm_csr_f32(rowptr, colind, C, B, A, M: int, K: int, N: int,
+                  stream=None) -> None:
+    """A[p - rowptr[0]] = <C_i, B_colind[p]> on the CSR pattern, fp32
+    (sddmm_csr_f32).  nnz is len(A), which must be rowptr[M] - rowptr[0]."""
+    torch = _torch()
+    dev = _check_sddmm(rowptr, colind, C, B, A, M, K, N, (torch.float32,))
+    _check(lib().sddmm_csr_f32(_ptr(rowptr), _ptr(colind), _ptr(C), _ptr(B),
+                               _ptr(A), M, K, N, A.numel(),
+                               _stream_handle(dev, stream)), "sddmm_csr_f32")
+
+
+def sddmm_csr_bf16in_f32acc(rowptr, colind, C, B, A, M: int, K: int, N: int,
+                            stream=None) -> None:
+    """SDDMM with bf16 C and B (torch.bfloat16 or int16/uint16 bits), fp32
+    accumulation and output (sddmm_csr_bf16in_f32acc)."""
+    torch = _torch()
+    bf = (torch.bfloat16, torch.int16, torch.uint16)
+    dev = _check_sddmm(rowptr, colind, C, B, A, M, K, N, bf)
+    _check(lib().sddmm_csr_bf16in_f32acc(_ptr(rowptr), _ptr(colind), _ptr(C),
+                                         _ptr(B), _ptr(A), M, K, N, A.numel(),
+                                         _stream_handle(dev, stream)),
+           "sddmm_csr_bf16in_f32acc")
+
+
+def sddmm(rowptr, colind, C, B, stream=None):
+    """Allocate A and compute the SDDMM values; the element type follows C.
+    rowptr[0] must be 0 (len(colind) entries)."""
+    torch = _torch()
+    M, N = C.shape
+    K = B.shape[0]
+    A = torch.empty(colind.numel(), dtype=torch.float32, device=C.device)
+    if C.dtype == torch.float32:
+        sddmm_csr_f32(rowptr, colind, C, B, A, M, K, N, stream)
+    else:
+        sddmm_csr_bf16in_f32acc(rowptr, colind, C, B, A, M, K, N, stream)
+    return A
 
 
 def resolve_tuning(dtype: int, N: int, tuning: Tuning | None = None) -> Tuning:

@@ -383,9 +383,85 @@ spmm_status_t run(int32_t dtype, const int32_t *rowptr, const int32_t *colind,
     return SPMM_SUCCESS;
 }
 
+// One SDDMM call: checks, then one launch (sddmm.hip).
+spmm_status_t run_sddmm(int32_t dtype, const int32_t *rowptr,
+                        const int32_t *colind, const void *C, const void *B,
+                        float *A, int64_t M, int64_t K, int64_t N, int64_t nnz,
+                        void *stream_ptr)
+{
+    g_last_error.clear();
+    if (dtype != SPMM_DTYPE_F32 && dtype != SPMM_DTYPE_BF16)
+        return fail(SPMM_ERROR_INVALID_VALUE, "unknown dtype");
+    if (M < 0 || K < 0 || N < 0 || nnz < 0)
+        return fail(SPMM_ERROR_INVALID_VALUE, "negative size");
+    if (M >= kMaxIndex || K >= kMaxIndex || N >= kMaxIndex || nnz >= kMaxIndex)
+        return fail(SPMM_ERROR_INVALID_VALUE, "M, K, N and nnz must be below 2^31");
+    if (nnz == 0)
+        return SPMM_SUCCESS;
+    if (M == 0)
+        return fail(SPMM_ERROR_INVALID_VALUE, "nnz > 0 with M == 0");
+    if (N == 0)
+        return fail(SPMM_ERROR_UNSUPPORTED, "N == 0 with stored entries");
+    if (rowptr == nullptr || colind == nullptr || C == nullptr || B == nullptr ||
+        A == nullptr)
+        return fail(SPMM_ERROR_INVALID_VALUE, "null pointer");
+    const uintptr_t esz = dtype == SPMM_DTYPE_BF16 ? 2 : 4;
+    if (((uintptr_t)C) % esz != 0 || ((uintptr_t)B) % esz != 0 ||
+        ((uintptr_t)A) % 4 != 0)
+        return fail(SPMM_ERROR_INVALID_VALUE, "operand not aligned to its element size");
+    SddmmArgs a;
+    a.dtype = dtype;
+    a.rowptr = rowptr;
+    a.colind = colind;
+    a.C = C;
+    a.B = B;
+    a.A = A;
+    a.M = M;
+    a.K = K;
+    a.N = N;
+    a.nnz = nnz;
+    hipStream_t stream = (hipStream_t)stream_ptr;
+    TimedCall tc{};
+    bool timing;
+    hipError_t err = hipSuccess;
+    {
+        std::lock_guard<std::mutex> lock(g_time_mu);
+        timing = g_timing;
+        if (timing &&
+            ((err = take_event(&tc.work0)) != hipSuccess ||
+             (err = take_event(&tc.work1)) != hipSuccess))
+            return fail_hip(err, "hipEventCreate");
+    }
+    err = launch_sddmm(a, stream, tc.work0, tc.work1);
+    if (err != hipSuccess)
+        return fail_hip(err, "sddmm kernel");
+    if (timing) {
+        std::lock_guard<std::mutex> lock(g_time_mu);
+        g_timed.push_back(tc);
+    }
+    return SPMM_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
+
+spmm_status_t sddmm_csr_f32(const int32_t *rowptr, const int32_t *colind,
+                            const float *C, const float *B, float *A,
+                            int64_t M, int64_t K, int64_t N, int64_t nnz,
+                            void *stream)
+{
+    return run_sddmm(SPMM_DTYPE_F32, rowptr, colind, C, B, A, M, K, N, nnz, stream);
+}
+
+spmm_status_t sddmm_csr_bf16in_f32acc(const int32_t *rowptr,
+                                      const int32_t *colind, const uint16_t *C,
+                                      const uint16_t *B, float *A, int64_t M,
+                                      int64_t K, int64_t N, int64_t nnz,
+                                      void *stream)
+{
+    return run_sddmm(SPMM_DTYPE_BF16, rowptr, colind, C, B, A, M, K, N, nnz, stream);
+}
 
 spmm_status_t spmm_csr_f32(const int32_t *rowptr, const int32_t *colind,
                            const float *vals, const float *B, float *C,

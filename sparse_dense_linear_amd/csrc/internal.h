@@ -108,6 +108,24 @@ struct WorkerArgs {
 hipError_t launch_worker(const WorkerConfig &cfg, const WorkerArgs &args,
                          hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
+// One SDDMM call (sddmm.hip): A[p - rowptr[0]] = <C_i, B_colind[p]>.
+struct SddmmArgs {
+    int dtype;               // SPMM_DTYPE_*: both dense operands
+    const int32_t *rowptr;
+    const int32_t *colind;
+    const void *C;           // M x N
+    const void *B;           // K x N
+    float *A;                // nnz values, CSR order
+    int64_t M;
+    int64_t K;
+    int64_t N;
+    int64_t nnz;             // rowptr[M] - rowptr[0]
+};
+
+// Enqueue one SDDMM launch; start/stop (may be null) are attached to it.
+hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream,
+                        hipEvent_t start, hipEvent_t stop);
+
 // Plain descriptors for the plan export.
 struct LongRow {
     int32_t row;
