@@ -95,15 +95,18 @@ def cpu_baseline(p, budget_s: float = 10.0, op: str = "spmm", dense=None) -> dic
     while True:
         if op == "spmm":
             oracle.spmm_ref(p.rowptr, p.colind, p.vals, p.B, p.N, with_bound=False)
-        else:
+        elif op == "sddmm":
             oracle.sddmm_ref(p.rowptr, p.colind, dense, p.B, p.N)
+        else:
+            oracle.fusedmm_ref(p.rowptr, p.colind, dense, p.B, p.B, p.N)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 1000:
             break
-    return {"value": round(flops(p) * reps / el / 1e9, 4), "unit": "GFLOP/s",
+    op_flops = flops(p) * (2 if op == "fusedmm" else 1)
+    return {"value": round(op_flops * reps / el / 1e9, 4), "unit": "GFLOP/s",
             "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"the whole {p.name} matrix ({'C only, no bound' if op == 'spmm' else 'SDDMM values and bound'}), "
+            "sample": f"the whole {p.name} matrix ({ {'spmm': 'C only, no bound', 'sddmm': 'SDDMM values and bound', 'fusedmm': 'FusedMM rows and bound'}[op]}), "
                       f"{reps} repetitions in {el:.1f} s"}
 
 
@@ -173,9 +176,10 @@ def main() -> int:
                     help="only run a 1 GiB device copy (for counter scaling)")
     ap.add_argument("--gather-ceiling", action="store_true",
                     help="only time the bare row-gather kernel and a device copy")
-    ap.add_argument("--op", default="spmm", choices=["spmm", "sddmm"],
+    ap.add_argument("--op", default="spmm", choices=["spmm", "sddmm", "fusedmm"],
                     help="spmm: C = A*B (the headline); sddmm: A = (C B^T) sampled "
-                         "on the workload's pattern, C drawn like B")
+                         "on the workload's pattern, C drawn like B; fusedmm: "
+                         "E = sum_p <C_i,B_j> D_j on the pattern (fp32 workloads)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -237,6 +241,18 @@ def main() -> int:
         def step():
             sfn(rowptr, colind, Cd, B, A, p.M, p.K, p.N, stream)
         op_flops, op_bytes = flops(p), sddmm_min_bytes(p)
+        if args.op == "fusedmm":
+            if p.dtype != "f32":
+                raise SystemExit("fusedmm runs on fp32 workloads")
+            Dd = torch.randn(p.K * p.N, dtype=torch.float32, device=dev,
+                             generator=torch.Generator(device=dev).manual_seed(8))
+            E = torch.empty(p.M * p.N, dtype=torch.float32, device=dev)
+
+            def step():  # noqa: F811
+                sdl.fusedmm_csr_f32(rowptr, colind, Cd, B, Dd, E, p.M, p.K, p.N,
+                                    p.nnz, stream)
+            op_flops = 2 * flops(p)
+            op_bytes = sddmm_min_bytes(p) - 4 * p.nnz + (p.K + p.M) * p.N * 4
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -285,7 +301,9 @@ def main() -> int:
     cold_med = float(np.median(cold)) if cold else None
 
     out = {
-        "metric": METRIC if args.op == "spmm" else METRIC.replace("SpMM", "SDDMM"),
+        "metric": METRIC if args.op == "spmm" else METRIC.replace(
+            "SpMM", {"sddmm": "SDDMM", "fusedmm": "FusedMM"}[args.op]).replace(
+            "2·nnz·N", "2·nnz·N" if args.op == "sddmm" else "4·nnz·N"),
         "value": round(gflops, 3),
         "unit": "GFLOP/s",
         "n_gpus": 1,
@@ -321,7 +339,7 @@ def main() -> int:
     }
     if not args.no_cpu:
         dense = None
-        if args.op == "sddmm":
+        if args.op in ("sddmm", "fusedmm"):
             dense = Cd.cpu().numpy()
             dense = dense.view(np.uint16) if p.dtype != "f32" else dense
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds, args.op, dense)

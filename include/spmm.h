@@ -201,6 +201,31 @@ spmm_status_t sddmm_csr_bf16in_f32acc(const int32_t *rowptr,
                                       void *stream);
 
 /*
+ * FusedMM on the pattern of a CSR matrix.  [IntelMax], the FusedMM
+ * operation (Fig. 6, Algorithm 3): the SDDMM value of each stored entry
+ * (row C_i times row B_j, as for sddmm_csr_f32) weights row D_j of a third
+ * dense matrix, summed per row:
+ *
+ *     E[i*N + n] = sum over p in row i of <C_i, B_colind[p]> * D[colind[p]*N + n]
+ *
+ *   C  M x N, B and D  K x N, E  M x N; all float32, row-major, leading
+ *   dimension exactly N (D has the N columns of C and B).
+ *   nnz = rowptr[M] - rowptr[0] (a precondition).
+ * E is overwritten; rows with no stored entries become zero rows.
+ *
+ * Two launches on `stream`: the SDDMM values are written to a stream-ordered
+ * scratch array of nnz floats (from the library's pool, released on the
+ * stream after use), and the sparse x dense product reads them as the values
+ * of A with D as its dense operand.  Errors and ownership as for the
+ * product; SPMM_ERROR_OUT_OF_MEMORY if the scratch array cannot be had.
+ * Numerics: each value is rounded to fp32 before it weights D_j.
+ */
+spmm_status_t fusedmm_csr_f32(const int32_t *rowptr, const int32_t *colind,
+                              const float *C, const float *B, const float *D,
+                              float *E, int64_t M, int64_t K, int64_t N,
+                              int64_t nnz, void *stream);
+
+/*
  * Health check for tests.  Inside a call, product wavefronts poll for the
  * plan entries they need while the plan workgroups of the same launch write
  * them; each poll is bounded (about a second), and an item whose entry

@@ -14,6 +14,8 @@ from ._binding import (  # noqa: F401
     DTYPE_F32,
     SpmmError,
     Tuning,
+    fusedmm,
+    fusedmm_csr_f32,
     lib,
     lib_path,
     plan_export,

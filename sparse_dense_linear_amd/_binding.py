@@ -79,7 +79,8 @@ def lib() -> ctypes.CDLL:
     L.spmm_stream_faults.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]
     L.sddmm_csr_f32.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
     L.sddmm_csr_bf16in_f32acc.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
-    for name in ("sddmm_csr_f32", "sddmm_csr_bf16in_f32acc"):
+    L.fusedmm_csr_f32.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
+    for name in ("sddmm_csr_f32", "sddmm_csr_bf16in_f32acc", "fusedmm_csr_f32"):
         getattr(L, name).restype = I32
     for name in ("spmm_csr_f32", "spmm_csr_bf16in_f32acc", "spmm_csr_tuned",
                  "spmm_resolve_tuning", "spmm_plan_export", "spmm_timing_enable",
@@ -259,6 +260,46 @@ def sddmm(rowptr, colind, C, B, stream=None):
     else:
         sddmm_csr_bf16in_f32acc(rowptr, colind, C, B, A, M, K, N, stream)
     return A
+
+
+def fusedmm_csr_f32(rowptr, colind, C, B, D, E, M: int, K: int, N: int,
+                    nnz: int, stream=None) -> None:
+    """E_i = sum_p <C_i, B_colind[p]> D_colind[p] over the CSR pattern, fp32
+    (fusedmm_csr_f32).  nnz must be rowptr[M] - rowptr[0]."""
+    torch = _torch()
+    dev = E.device
+    for name, t in {"rowptr": rowptr, "colind": colind, "C": C, "B": B, "D": D,
+                    "E": E}.items():
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device != dev or dev.type != "cuda":
+            raise ValueError(f"{name} must live on the same GPU as E")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if rowptr.dtype != torch.int32 or colind.dtype != torch.int32:
+        raise TypeError("rowptr and colind must be int32")
+    for name, t in {"C": C, "B": B, "D": D, "E": E}.items():
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if rowptr.numel() != M + 1:
+        raise ValueError("rowptr must hold M+1 entries")
+    if C.numel() != M * N or B.numel() != K * N or D.numel() != K * N or E.numel() != M * N:
+        raise ValueError("C and E must hold M*N, B and D K*N elements")
+    if nnz < 0 or nnz > colind.numel():
+        raise ValueError("nnz must be in [0, len(colind)]")
+    _check(lib().fusedmm_csr_f32(_ptr(rowptr), _ptr(colind), _ptr(C), _ptr(B),
+                                 _ptr(D), _ptr(E), M, K, N, nnz,
+                                 _stream_handle(dev, stream)), "fusedmm_csr_f32")
+
+
+def fusedmm(rowptr, colind, C, B, D, stream=None):
+    """Allocate E and compute FusedMM (rowptr[0] must be 0)."""
+    torch = _torch()
+    M, N = C.shape
+    K = B.shape[0]
+    E = torch.empty((M, N), dtype=torch.float32, device=C.device)
+    fusedmm_csr_f32(rowptr, colind, C, B, D, E, M, K, N, colind.numel(), stream)
+    return E
 
 
 def resolve_tuning(dtype: int, N: int, tuning: Tuning | None = None) -> Tuning:

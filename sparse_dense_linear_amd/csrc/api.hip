@@ -314,12 +314,15 @@ spmm_status_t check_args(int32_t dtype, const int32_t *rowptr, const void *B,
     return SPMM_SUCCESS;
 }
 
-spmm_status_t run(int32_t dtype, const int32_t *rowptr, const int32_t *colind,
-                  const void *vals, const void *B, float *C, int64_t M,
-                  int64_t K, int64_t N, const spmm_tuning_t *tuning,
-                  void *stream_ptr)
+// The product on `stream`; the launch carries e0/e1 when given (the
+// caller then records them), else this call's timing events if enabled.
+spmm_status_t run_with(int32_t dtype, const int32_t *rowptr,
+                       const int32_t *colind, const void *vals, const void *B,
+                       float *C, int64_t M, int64_t K, int64_t N,
+                       const spmm_tuning_t *tuning, void *stream_ptr,
+                       bool own_events, hipEvent_t e0, hipEvent_t e1,
+                       bool vals_relative = false)
 {
-    g_last_error.clear();
     spmm_status_t st = check_args(dtype, rowptr, B, C, M, K, N);
     if (st != SPMM_SUCCESS)
         return st;
@@ -347,8 +350,11 @@ spmm_status_t run(int32_t dtype, const int32_t *rowptr, const int32_t *colind,
         return fail_hip(err, "scratch allocation");
 
     TimedCall tc{};
-    bool timing;
-    {
+    bool timing = false;
+    if (own_events) {
+        tc.work0 = e0;
+        tc.work1 = e1;
+    } else {
         std::lock_guard<std::mutex> lock(g_time_mu);
         timing = g_timing;
         if (timing &&
@@ -361,6 +367,7 @@ spmm_status_t run(int32_t dtype, const int32_t *rowptr, const int32_t *colind,
     wa.rowptr = rowptr;
     wa.colind = colind;
     wa.vals = vals;
+    wa.vals_relative = vals_relative ? 1 : 0;
     wa.B = B;
     wa.C = C;
     wa.M = M;
@@ -382,6 +389,22 @@ spmm_status_t run(int32_t dtype, const int32_t *rowptr, const int32_t *colind,
     }
     return SPMM_SUCCESS;
 }
+
+spmm_status_t run(int32_t dtype, const int32_t *rowptr, const int32_t *colind,
+                  const void *vals, const void *B, float *C, int64_t M,
+                  int64_t K, int64_t N, const spmm_tuning_t *tuning,
+                  void *stream_ptr)
+{
+    g_last_error.clear();
+    return run_with(dtype, rowptr, colind, vals, B, C, M, K, N, tuning,
+                    stream_ptr, false, nullptr, nullptr);
+}
+
+spmm_status_t launch_sddmm_checked(int32_t dtype, const int32_t *rowptr,
+                                   const int32_t *colind, const void *C,
+                                   const void *B, float *A, int64_t M,
+                                   int64_t K, int64_t N, int64_t nnz,
+                                   void *stream_ptr);
 
 // One SDDMM call: checks, then one launch (sddmm.hip).
 spmm_status_t run_sddmm(int32_t dtype, const int32_t *rowptr,
@@ -409,6 +432,16 @@ spmm_status_t run_sddmm(int32_t dtype, const int32_t *rowptr,
     if (((uintptr_t)C) % esz != 0 || ((uintptr_t)B) % esz != 0 ||
         ((uintptr_t)A) % 4 != 0)
         return fail(SPMM_ERROR_INVALID_VALUE, "operand not aligned to its element size");
+    return launch_sddmm_checked(dtype, rowptr, colind, C, B, A, M, K, N, nnz,
+                                stream_ptr);
+}
+
+spmm_status_t launch_sddmm_checked(int32_t dtype, const int32_t *rowptr,
+                                   const int32_t *colind, const void *C,
+                                   const void *B, float *A, int64_t M,
+                                   int64_t K, int64_t N, int64_t nnz,
+                                   void *stream_ptr)
+{
     SddmmArgs a;
     a.dtype = dtype;
     a.rowptr = rowptr;
@@ -442,9 +475,96 @@ spmm_status_t run_sddmm(int32_t dtype, const int32_t *rowptr,
     return SPMM_SUCCESS;
 }
 
+// FusedMM: E_i = sum_p <C_i, B_j> D_j.  The SDDMM values go to a
+// stream-ordered scratch array of nnz floats, which the product kernel
+// then reads as the values of A with D as its dense operand: two launches
+// on the stream, the values making one round trip through memory.
+spmm_status_t run_fusedmm(const int32_t *rowptr, const int32_t *colind,
+                          const float *C, const float *B, const float *D,
+                          float *E, int64_t M, int64_t K, int64_t N,
+                          int64_t nnz, void *stream_ptr)
+{
+    g_last_error.clear();
+    if (M < 0 || K < 0 || N < 0 || nnz < 0)
+        return fail(SPMM_ERROR_INVALID_VALUE, "negative size");
+    if (M >= kMaxIndex || K >= kMaxIndex || N >= kMaxIndex || nnz >= kMaxIndex)
+        return fail(SPMM_ERROR_INVALID_VALUE, "M, K, N and nnz must be below 2^31");
+    if (M == 0 || N == 0)
+        return SPMM_SUCCESS;
+    if (rowptr == nullptr || E == nullptr || (nnz > 0 && (colind == nullptr ||
+        C == nullptr || B == nullptr || D == nullptr)))
+        return fail(SPMM_ERROR_INVALID_VALUE, "null pointer");
+    if ((((uintptr_t)C) | ((uintptr_t)B) | ((uintptr_t)D) | ((uintptr_t)E)) % 4 != 0)
+        return fail(SPMM_ERROR_INVALID_VALUE, "operand not aligned to its element size");
+    hipStream_t stream = (hipStream_t)stream_ptr;
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return fail_hip(err, "hipGetDevice");
+    hipMemPool_t pool;
+    if ((err = pool_for_device(dev, &pool)) != hipSuccess)
+        return fail_hip(err, "memory pool");
+    float *vals = nullptr;
+    const size_t bytes = (size_t)(nnz > 0 ? nnz : 1) * sizeof(float);
+    if (test_fail_alloc())
+        return fail(SPMM_ERROR_OUT_OF_MEMORY, "allocation failure forced by SPMM_TEST_FAIL_ALLOC");
+    err = hipMallocFromPoolAsync((void **)&vals, bytes, pool, stream);
+    if (err == hipErrorOutOfMemory)
+        return fail(SPMM_ERROR_OUT_OF_MEMORY, "value scratch allocation failed");
+    if (err != hipSuccess)
+        return fail_hip(err, "value scratch allocation");
+
+    TimedCall tc{};
+    bool timing;
+    {
+        std::lock_guard<std::mutex> lock(g_time_mu);
+        timing = g_timing;
+        if (timing &&
+            ((err = take_event(&tc.work0)) != hipSuccess ||
+             (err = take_event(&tc.work1)) != hipSuccess)) {
+            hipFreeAsync(vals, stream);
+            return fail_hip(err, "hipEventCreate");
+        }
+    }
+    spmm_status_t st = SPMM_SUCCESS;
+    if (nnz > 0) {
+        SddmmArgs a;
+        a.dtype = SPMM_DTYPE_F32;
+        a.rowptr = rowptr;
+        a.colind = colind;
+        a.C = C;
+        a.B = B;
+        a.A = vals;
+        a.M = M;
+        a.K = K;
+        a.N = N;
+        a.nnz = nnz;
+        if ((err = launch_sddmm(a, stream, tc.work0, nullptr)) != hipSuccess)
+            st = fail_hip(err, "sddmm kernel");
+    }
+    if (st == SPMM_SUCCESS)
+        st = run_with(SPMM_DTYPE_F32, rowptr, colind, vals, D, E, M, K, N, nullptr,
+                      stream_ptr, true, nnz > 0 ? nullptr : tc.work0, tc.work1,
+                      true);
+    hipFreeAsync(vals, stream);
+    if (st == SPMM_SUCCESS && timing) {
+        std::lock_guard<std::mutex> lock(g_time_mu);
+        g_timed.push_back(tc);
+    }
+    return st;
+}
+
 }  // namespace
 
 extern "C" {
+
+spmm_status_t fusedmm_csr_f32(const int32_t *rowptr, const int32_t *colind,
+                              const float *C, const float *B, const float *D,
+                              float *E, int64_t M, int64_t K, int64_t N,
+                              int64_t nnz, void *stream)
+{
+    return run_fusedmm(rowptr, colind, C, B, D, E, M, K, N, nnz, stream);
+}
 
 spmm_status_t sddmm_csr_f32(const int32_t *rowptr, const int32_t *colind,
                             const float *C, const float *B, float *A,

@@ -90,7 +90,8 @@ WorkerConfig choose_worker(int dtype, int64_t N, const void *B, const float *C);
 struct WorkerArgs {
     const int32_t *rowptr;
     const int32_t *colind;
-    const void *vals;
+    const void *vals;      // value of entry p at vals[p] (or vals[p - rowptr[0]])
+    int32_t vals_relative; // 1: vals is indexed from rowptr[0], not from 0
     const void *B;
     float *C;              // null: plan only (no product)
     int64_t M;

@@ -657,6 +657,8 @@ template <class S>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4)))
 void call_kernel(WorkerArgs a, ProductShape ps)
 {
+    if (a.vals_relative)  // entry p's value sits at vals[p - rowptr[0]]
+        a.vals = (const char *)a.vals - (int64_t)a.rowptr[0] * S::ESZ;
     __shared__ union {
         WaveStage stage[kWavesPerBlock];
         PlanBlockLds plan;

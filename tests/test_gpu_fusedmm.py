@@ -1,0 +1,140 @@
+"""GPU parity of the FusedMM entry point against the fp64 oracle.
+
+Page: [IntelMax] "Performance Optimization of Deep Learning Sparse Matrix
+Kernels on Intel Max Series GPU", the FusedMM operation (Fig. 6,
+Algorithm 3).
+
+Bar: |E_gpu - E_ref| <= 2 tol(N) T + 1e-6 per element, with the bound
+T[i,n] = sum_p S_p |D_jn| and tol(N) = max(1e-5, N 2^-23): each SDDMM value
+is off by at most ~N 2^-24 S_p before it weights D_j (its rounding to fp32
+adds 2^-24 |a_p|), and the sum over the row adds the product's own fp32
+rounding, bounded the same way as the product's tests bound it.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_dense_linear_amd as sdl
+import workloads as W
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def tol(N):
+    return 2 * max(1e-5, N * 2.0 ** -23)
+
+
+def run_fused(rowptr, colind, C, B, D, M, K, N, fill=float("nan")):
+    rp = torch.from_numpy(np.ascontiguousarray(rowptr, np.int32)).cuda()
+    ci = torch.from_numpy(np.ascontiguousarray(colind, np.int32)).cuda()
+    E = torch.full((M * N,), fill, dtype=torch.float32, device="cuda")
+    nnz = int(rowptr[-1]) - int(rowptr[0])
+    sdl.fusedmm_csr_f32(rp, ci, torch.from_numpy(C).cuda(), torch.from_numpy(B).cuda(),
+                        torch.from_numpy(D).cuda(), E, M, K, N, nnz)
+    torch.cuda.synchronize()
+    assert sdl.stream_faults() == 0
+    return E.cpu().numpy().reshape(M, N)
+
+
+def check(rowptr, colind, C, B, D, M, K, N, what=""):
+    E = run_fused(rowptr, colind, C, B, D, M, K, N)
+    Eref, T = oracle.fusedmm_ref(rowptr, colind, C, B, D, N)
+    bad = ~(np.abs(E.astype(np.float64) - Eref) <= tol(N) * T + 1e-6)
+    if bad.any():
+        i, n = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {int(bad.sum())} of {E.size} outside the bound; "
+                             f"first ({i},{n}): gpu={E[i, n]!r} ref={Eref[i, n]!r} T={T[i, n]!r}")
+    return E
+
+
+def pattern(lengths, K, seed):
+    rng = np.random.default_rng(seed)
+    lengths = np.asarray(lengths, np.int64)
+    rowptr = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    colind = np.concatenate([np.sort(rng.choice(K, int(l), replace=False))
+                             if l else np.zeros(0, np.int64) for l in lengths]).astype(np.int32)
+    return rowptr, colind
+
+
+def dense(rng, rows, N):
+    return rng.uniform(-1, 1, (rows, N)).astype(np.float32)
+
+
+def test_worked_example_bitwise():
+    g = json.load(open(os.path.join(GOLDEN, "worked_example_fig3_fig6.json")))
+    f = lambda k: np.array(g[k], np.float32)
+    E = run_fused(np.array(g["rowptr"]), np.array(g["colind"]), f("C"), f("B"), f("D"),
+                  g["M"], g["K"], g["N"])
+    assert np.array_equal(E, f("E"))
+
+
+EDGE = [0, 1, 2, 3, 9, 16, 17, 64, 200, 257, 1100, 3000]
+
+
+@pytest.mark.parametrize("N", [1, 4, 8, 32, 64, 128, 256, 512])
+def test_edge_rows(N):
+    """Rows of every kind the product routes (empty, short, medium, long
+    rows cut into chunks)."""
+    rng = np.random.default_rng(N + 100)
+    M, K = 200, 4000
+    lengths = rng.choice(EDGE, size=M)
+    lengths[:len(EDGE)] = EDGE
+    rp, ci = pattern(lengths, K, seed=N)
+    check(rp, ci, dense(rng, M, N), dense(rng, K, N), dense(rng, K, N), M, K, N, f"N={N}")
+
+
+def test_view_and_empty():
+    rng = np.random.default_rng(3)
+    M, K, N = 300, 700, 64
+    lengths = rng.integers(0, 30, M)
+    lengths[::7] = 0
+    rp, ci = pattern(lengths, K, seed=3)
+    C, B, D = dense(rng, M, N), dense(rng, K, N), dense(rng, K, N)
+    E0 = check(rp, ci, C, B, D, M, K, N)
+    assert np.array_equal(E0[lengths == 0], np.zeros(((lengths == 0).sum(), N), np.float32))
+    pad = 5
+    E1 = run_fused(rp + pad, np.concatenate([np.zeros(pad, np.int32), ci]), C, B, D, M, K, N)
+    assert np.array_equal(E1[lengths <= 64], E0[lengths <= 64])
+
+
+def test_no_entries():
+    rng = np.random.default_rng(4)
+    M, K, N = 50, 10, 16
+    E = run_fused(np.zeros(M + 1, np.int32), np.zeros(0, np.int32), dense(rng, M, N),
+                  dense(rng, K, N), dense(rng, K, N), M, K, N)
+    assert np.array_equal(E, np.zeros((M, N), np.float32))
+
+
+def test_equals_sddmm_then_spmm():
+    """The fused call equals, bit for bit, SDDMM into an array followed by
+    the product with those values (the same kernels in the same order)."""
+    rng = np.random.default_rng(5)
+    M, K, N = 1500, 1200, 64
+    rp, ci = pattern(rng.integers(0, 40, M), K, seed=5)
+    C, B, D = dense(rng, M, N), dense(rng, K, N), dense(rng, K, N)
+    E = run_fused(rp, ci, C, B, D, M, K, N)
+    rpt, cit = torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda()
+    A = torch.empty(ci.size, dtype=torch.float32, device="cuda")
+    sdl.sddmm_csr_f32(rpt, cit, torch.from_numpy(C).cuda(), torch.from_numpy(B).cuda(),
+                      A, M, K, N)
+    E2 = torch.empty(M * N, dtype=torch.float32, device="cuda")
+    sdl.spmm_csr_f32(rpt, cit, A, torch.from_numpy(D).cuda(), E2, M, K, N)
+    torch.cuda.synchronize()
+    single = np.diff(rp) <= sdl.resolve_tuning(0, N).medium_max
+    assert np.array_equal(E[single], E2.cpu().numpy().reshape(M, N)[single])
+
+
+def test_powerlaw_pattern():
+    """FusedMM on the power-law workload's pattern (N = 64), every element."""
+    p = W.make("powerlaw_262k_n64")
+    rng = np.random.default_rng(6)
+    C = rng.standard_normal((p.M, p.N)).astype(np.float32)
+    D = rng.standard_normal((p.K, p.N)).astype(np.float32)
+    check(p.rowptr, p.colind, C, p.B.reshape(p.K, p.N), D, p.M, p.K, p.N, "powerlaw")
