@@ -18,7 +18,10 @@ HEADER = os.path.join(ROOT, "include", "spmm.h")
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(spmm_\w+)\s*\(", text)))
+    # every function declaration: a return type, a name, an opening paren
+    names = re.findall(r"^\s*(?:spmm_status_t|const\s+char\s*\*)\s*(\w+)\s*\(",
+                       text, re.M)
+    return sorted(set(names))
 
 
 def test_header_declares_entry_points():
@@ -26,7 +29,8 @@ def test_header_declares_entry_points():
     for must in ("spmm_csr_f32", "spmm_csr_bf16in_f32acc", "spmm_csr_tuned",
                  "spmm_resolve_tuning", "spmm_plan_export", "spmm_status_string",
                  "spmm_last_error", "spmm_timing_enable", "spmm_timing_read",
-                 "spmm_stream_faults"):
+                 "spmm_stream_faults", "sddmm_csr_f32", "sddmm_csr_bf16in_f32acc",
+                 "fusedmm_csr_f32"):
         assert must in names
 
 
@@ -159,3 +163,58 @@ def test_binding_checks_operands():
     f = torch.zeros(4, dtype=torch.float32)
     with pytest.raises((ValueError, TypeError)):
         sdl.spmm_csr_f32(t, t, f, f, f, 3, 2, 2)
+
+
+@pytest.mark.parametrize("M,K,N,nnz,rowptr,C,B,A,expect", [
+    (-1, 4, 4, 4, FAKE, FAKE, FAKE, FAKE, 1),         # negative M
+    (4, 4, 4, -1, FAKE, FAKE, FAKE, FAKE, 1),         # negative nnz
+    (4, 4, 4, 2 ** 31, FAKE, FAKE, FAKE, FAKE, 1),    # nnz too large
+    (0, 4, 4, 3, FAKE, FAKE, FAKE, FAKE, 1),          # entries without rows
+    (4, 4, 0, 3, FAKE, FAKE, FAKE, FAKE, 4),          # N == 0 with entries
+    (4, 4, 4, 3, None, FAKE, FAKE, FAKE, 1),          # rowptr null
+    (4, 4, 4, 3, FAKE, None, FAKE, FAKE, 1),          # C null
+    (4, 4, 4, 3, FAKE, FAKE, FAKE, None, 1),          # A null
+    (4, 4, 4, 3, FAKE, FAKE + 2, FAKE, FAKE, 1),      # C misaligned
+    (4, 4, 4, 3, FAKE, FAKE, FAKE, FAKE + 1, 1),      # A misaligned
+    (4, 4, 4, 0, None, None, None, None, 0),          # no entries: nothing to do
+])
+def test_sddmm_host_validation(M, K, N, nnz, rowptr, C, B, A, expect):
+    rc = raw_call("sddmm_csr_f32", rowptr, FAKE, C, B, A, M, K, N, nnz, None)
+    assert rc == expect, sdl.lib().spmm_last_error()
+
+
+def test_sddmm_bf16_alignment():
+    rc = raw_call("sddmm_csr_bf16in_f32acc", FAKE, FAKE, FAKE + 1, FAKE, FAKE,
+                  4, 4, 4, 3, None)
+    assert rc == 1
+
+
+@pytest.mark.parametrize("M,K,N,nnz,rowptr,E,D,expect", [
+    (-1, 4, 4, 4, FAKE, FAKE, FAKE, 1),      # negative M
+    (4, 4, 4, 2 ** 31, FAKE, FAKE, FAKE, 1),  # nnz too large
+    (4, 4, 4, 3, None, FAKE, FAKE, 1),       # rowptr null
+    (4, 4, 4, 3, FAKE, None, FAKE, 1),       # E null
+    (4, 4, 4, 3, FAKE, FAKE, None, 1),       # D null with entries
+    (4, 4, 4, 3, FAKE, FAKE + 2, FAKE, 1),   # E misaligned
+    (0, 4, 4, 0, None, None, None, 0),       # M == 0: nothing to do
+    (4, 4, 0, 0, None, None, None, 0),       # N == 0: nothing to do
+])
+def test_fusedmm_host_validation(M, K, N, nnz, rowptr, E, D, expect):
+    rc = raw_call("fusedmm_csr_f32", rowptr, FAKE, FAKE, FAKE, D, E, M, K, N, nnz, None)
+    assert rc == expect, sdl.lib().spmm_last_error()
+
+
+def test_fusedmm_forced_allocation_failure(monkeypatch):
+    monkeypatch.setenv("SPMM_TEST_FAIL_ALLOC", "1")
+    rc = raw_call("fusedmm_csr_f32", FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 4, 3, None)
+    # without a GPU the device query fails first; with one, the forced failure
+    assert rc in (2, 3)
+
+
+def test_sddmm_binding_checks_operands():
+    t = torch.zeros(4, dtype=torch.int32)
+    f = torch.zeros(4, dtype=torch.float32)
+    with pytest.raises((ValueError, TypeError)):
+        sdl.sddmm_csr_f32(t, t, f, f, f, 3, 2, 2)
+    with pytest.raises((ValueError, TypeError)):
+        sdl.fusedmm_csr_f32(t, t, f, f, f, f, 3, 2, 2, 4)
