@@ -176,6 +176,9 @@ def main() -> int:
                     help="only run a 1 GiB device copy (for counter scaling)")
     ap.add_argument("--gather-ceiling", action="store_true",
                     help="only time the bare row-gather kernel and a device copy")
+    ap.add_argument("--n", type=int, default=None,
+                    help="spmm only: dense width N in place of the workload's "
+                         "(B drawn N(0,1) fp32 on the same pattern)")
     ap.add_argument("--op", default="spmm", choices=["spmm", "sddmm", "fusedmm"],
                     help="spmm: C = A*B (the headline); sddmm: A = (C B^T) sampled "
                          "on the workload's pattern, C drawn like B; fusedmm: "
@@ -212,6 +215,13 @@ def main() -> int:
         return 0
 
     p = W.make(args.workload)
+    if args.n is not None and args.n != p.N:
+        if args.op != "spmm" or p.dtype != "f32":
+            raise SystemExit("--n applies to the fp32 product only")
+        rng = np.random.default_rng(args.n)
+        p = W.CsrProblem(f"{p.name}_as_n{args.n}", p.M, p.K, args.n, p.rowptr, p.colind,
+                         p.vals, rng.standard_normal((p.K, args.n)).astype(np.float32),
+                         p.dtype, {**p.meta, "n_override": args.n})
     rowptr = torch.from_numpy(p.rowptr).to(dev)
     colind = torch.from_numpy(p.colind).to(dev)
     if p.dtype == "f32":

@@ -798,6 +798,8 @@ hipError_t launch_vec(int group, int nv, const WorkerArgs &a, hipStream_t s,
                       hipEvent_t e0, hipEvent_t e1)
 {
     switch (group) {
+    case 1: return launch_shape<Shape<DT, VEC, 1, 1, BUF>>(a, s, e0, e1);
+    case 2: return launch_shape<Shape<DT, VEC, 2, 1, BUF>>(a, s, e0, e1);
     case 4: return launch_shape<Shape<DT, VEC, 4, 1, BUF>>(a, s, e0, e1);
     case 8: return launch_shape<Shape<DT, VEC, 8, 1, BUF>>(a, s, e0, e1);
     case 16: return launch_shape<Shape<DT, VEC, 16, 1, BUF>>(a, s, e0, e1);
@@ -826,7 +828,11 @@ WorkerConfig choose_worker(int dtype, int64_t N, const void *B, const float *C)
             break;
     }
     const int64_t vecs = (N + vec - 1) / vec;  // lane vectors per B row
-    int group = 4;  // at least 4 lanes per row group
+    // The narrowest power-of-two group that covers a row with one vector per
+    // lane: small N (one or two vectors per row) gets groups of 1 or 2 lanes
+    // and 64 or 32 rows per wavefront, instead of lanes that would only
+    // repeat a neighbour's load.
+    int group = 1;
     while (group < 64 && group < vecs)
         group *= 2;
     int64_t nv = (vecs + group - 1) / group;

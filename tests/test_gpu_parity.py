@@ -342,3 +342,12 @@ def test_scaled_workloads(name, make):
     C = run_gpu(p)
     Cref, Sref = reference(p)
     assert_parity(C, Cref, Sref, p.dtype, name)
+
+
+@pytest.mark.parametrize("N", [1, 2, 4, 6, 8, 12, 16])
+def test_small_n_powerlaw(N):
+    """Small N (groups of 1 or 2 lanes, 64 or 32 rows per wavefront) on a
+    scaled power-law pattern, every element."""
+    p = W.powerlaw_rows(M=32768, N=N, seed=40 + N)
+    Cref, Sref = reference(p)
+    assert_parity(run_gpu(p), Cref, Sref, "f32", f"N={N}")
