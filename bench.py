@@ -41,6 +41,9 @@ METRIC = ("SpMM GFLOP/s (2·nnz·N) and effective HBM GB/s as % of peak, "
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "powerlaw_262k_n64"
 KERNEL_SOURCES = ["sparse_dense_linear_amd/csrc/worker.hip",
+                  "sparse_dense_linear_amd/csrc/eb.hip",
+                  "sparse_dense_linear_amd/csrc/gather.h",
+                  "sparse_dense_linear_amd/csrc/span.h",
                   "sparse_dense_linear_amd/csrc/sddmm.hip",
                   "sparse_dense_linear_amd/csrc/plan_device.h",
                   "sparse_dense_linear_amd/csrc/plan.hip",
@@ -93,7 +96,7 @@ def cpu_baseline(p, budget_s: float = 10.0, op: str = "spmm", dense=None) -> dic
     reps = 0
     t0 = time.perf_counter()
     while True:
-        if op == "spmm":
+        if op in ("spmm", "eb"):
             oracle.spmm_ref(p.rowptr, p.colind, p.vals, p.B, p.N, with_bound=False)
         elif op == "sddmm":
             oracle.sddmm_ref(p.rowptr, p.colind, dense, p.B, p.N)
@@ -106,7 +109,7 @@ def cpu_baseline(p, budget_s: float = 10.0, op: str = "spmm", dense=None) -> dic
     op_flops = flops(p) * (2 if op == "fusedmm" else 1)
     return {"value": round(op_flops * reps / el / 1e9, 4), "unit": "GFLOP/s",
             "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"the whole {p.name} matrix ({ {'spmm': 'C only, no bound', 'sddmm': 'SDDMM values and bound', 'fusedmm': 'FusedMM rows and bound'}[op]}), "
+            "sample": f"the whole {p.name} matrix ({ {'spmm': 'C only, no bound', 'eb': 'C only, no bound', 'sddmm': 'SDDMM values and bound', 'fusedmm': 'FusedMM rows and bound'}[op]}), "
                       f"{reps} repetitions in {el:.1f} s"}
 
 
@@ -179,8 +182,9 @@ def main() -> int:
     ap.add_argument("--n", type=int, default=None,
                     help="spmm only: dense width N in place of the workload's "
                          "(B drawn N(0,1) fp32 on the same pattern)")
-    ap.add_argument("--op", default="spmm", choices=["spmm", "sddmm", "fusedmm"],
-                    help="spmm: C = A*B (the headline); sddmm: A = (C B^T) sampled "
+    ap.add_argument("--op", default="spmm", choices=["spmm", "eb", "sddmm", "fusedmm"],
+                    help="spmm: C = A*B (the headline); eb: the same product by the "
+                         "element-balanced kernel; sddmm: A = (C B^T) sampled "
                          "on the workload's pattern, C drawn like B; fusedmm: "
                          "E = sum_p <C_i,B_j> D_j on the pattern (fp32 workloads)")
     args = ap.parse_args()
@@ -233,11 +237,16 @@ def main() -> int:
         B = torch.from_numpy(p.B.reshape(-1).view(np.int16)).to(dev)
         fn = sdl.spmm_csr_bf16in_f32acc
     stream = torch.cuda.current_stream(dev)
-    if args.op == "spmm":
+    if args.op in ("spmm", "eb"):
         C = torch.empty(p.M * p.N, dtype=torch.float32, device=dev)
+        if args.op == "spmm":
+            def step():
+                fn(rowptr, colind, vals, B, C, p.M, p.K, p.N, stream)
+        else:
+            dt = sdl.DTYPE_F32 if p.dtype == "f32" else sdl.DTYPE_BF16
 
-        def step():
-            fn(rowptr, colind, vals, B, C, p.M, p.K, p.N, stream)
+            def step():
+                sdl.spmm_csr_eb(dt, rowptr, colind, vals, B, C, p.M, p.K, p.N, stream)
         op_flops, op_bytes = flops(p), min_bytes(p)
     else:
         # dense left operand: M x N, same element type and recipe as B
@@ -311,7 +320,7 @@ def main() -> int:
     cold_med = float(np.median(cold)) if cold else None
 
     out = {
-        "metric": METRIC if args.op == "spmm" else METRIC.replace(
+        "metric": METRIC if args.op in ("spmm", "eb") else METRIC.replace(
             "SpMM", {"sddmm": "SDDMM", "fusedmm": "FusedMM"}[args.op]).replace(
             "2·nnz·N", "2·nnz·N" if args.op == "sddmm" else "4·nnz·N"),
         "value": round(gflops, 3),

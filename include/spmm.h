@@ -167,6 +167,24 @@ spmm_status_t spmm_timing_read(double *plan_ms, double *worker_ms,
                                int64_t *calls);
 
 /*
+ * The same product C = A * B (either element type), computed by the
+ * element-balanced kernel instead of the row plan: [Sgap] "Sgap: Towards
+ * Efficient Sparse Tensor Algebra Compilation for GPU", the element-balanced
+ * points of atomic parallelism and the grouped segmented reduction.  The
+ * stored entries are split into equal spans, one per wavefront; partial sums
+ * of entries that share a row are combined across lane groups in entry
+ * order, and the rows cut by span ends go through carry slots that a second
+ * launch adds up in order, so results repeat bit for bit (no atomics).
+ * Arguments, layout, ownership and errors as for spmm_csr_tuned (dtype is
+ * SPMM_DTYPE_F32 or SPMM_DTYPE_BF16); the carry slots (2 rows of N floats
+ * per wavefront of the GPU) are kept per stream by the library.
+ */
+spmm_status_t spmm_csr_eb(int32_t dtype, const int32_t *rowptr,
+                          const int32_t *colind, const void *vals,
+                          const void *B, float *C, int64_t M, int64_t K,
+                          int64_t N, void *stream);
+
+/*
  * Sampled dense-dense product (SDDMM) on the pattern of a CSR matrix.
  * [IntelMax] "Performance Optimization of Deep Learning Sparse Matrix
  * Kernels on Intel Max Series GPU", the SDDMM operation (Fig. 3, Algorithm
@@ -213,10 +231,10 @@ spmm_status_t sddmm_csr_bf16in_f32acc(const int32_t *rowptr,
  *   nnz = rowptr[M] - rowptr[0] (a precondition).
  * E is overwritten; rows with no stored entries become zero rows.
  *
- * Two launches on `stream`: the SDDMM values are written to a stream-ordered
- * scratch array of nnz floats (from the library's pool, released on the
- * stream after use), and the sparse x dense product reads them as the values
- * of A with D as its dense operand.  Errors and ownership as for the
+ * Two launches on `stream`: the SDDMM values are written to a scratch array
+ * of nnz floats (kept per stream by the library, from its stream-ordered
+ * pool, grown when a call needs more), and the sparse x dense product reads
+ * them as the values of A with D as its dense operand.  Errors and ownership as for the
  * product; SPMM_ERROR_OUT_OF_MEMORY if the scratch array cannot be had.
  * Numerics: each value is rounded to fp32 before it weights D_j.
  */

@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     sddmm_csr_f32,
     spmm,
     spmm_csr_bf16in_f32acc,
+    spmm_csr_eb,
     spmm_csr_f32,
     spmm_csr_tuned,
     status_string,

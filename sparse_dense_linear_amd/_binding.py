@@ -80,7 +80,9 @@ def lib() -> ctypes.CDLL:
     L.sddmm_csr_f32.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
     L.sddmm_csr_bf16in_f32acc.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
     L.fusedmm_csr_f32.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
-    for name in ("sddmm_csr_f32", "sddmm_csr_bf16in_f32acc", "fusedmm_csr_f32"):
+    L.spmm_csr_eb.argtypes = [I32, P, P, P, P, P, I64, I64, I64, P]
+    for name in ("sddmm_csr_f32", "sddmm_csr_bf16in_f32acc", "fusedmm_csr_f32",
+                 "spmm_csr_eb"):
         getattr(L, name).restype = I32
     for name in ("spmm_csr_f32", "spmm_csr_bf16in_f32acc", "spmm_csr_tuned",
                  "spmm_resolve_tuning", "spmm_plan_export", "spmm_timing_enable",
@@ -184,6 +186,20 @@ def spmm_csr_tuned(dtype: int, rowptr, colind, vals, B, C, M: int, K: int,
                                 _ptr(B), _ptr(C), M, K, N, ts,
                                 _stream_handle(dev, stream)),
            "spmm_csr_tuned")
+
+
+def spmm_csr_eb(dtype: int, rowptr, colind, vals, B, C, M: int, K: int,
+                N: int, stream=None) -> None:
+    """C = A * B by the element-balanced kernel (spmm_csr_eb)."""
+    torch = _torch()
+    if dtype == DTYPE_F32:
+        vd = bd = (torch.float32,)
+    else:
+        vd = bd = (torch.bfloat16, torch.int16, torch.uint16)
+    dev = _check_operands(rowptr, colind, vals, B, C, M, K, N, vd, bd)
+    _check(lib().spmm_csr_eb(dtype, _ptr(rowptr), _ptr(colind), _ptr(vals), _ptr(B),
+                             _ptr(C), M, K, N, _stream_handle(dev, stream)),
+           "spmm_csr_eb")
 
 
 def spmm(rowptr, colind, vals, B, M: int | None = None, stream=None):

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libsdl_spmm.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["api.hip", "plan.hip", "worker.hip", "sddmm.hip"]
+SOURCES = ["api.hip", "plan.hip", "worker.hip", "sddmm.hip", "eb.hip"]
 CEILING_SOURCE = "ceiling.hip"
 CEILING_PATH = os.path.join(HERE, "libsdl_ceiling.so")
 ARCH = "gfx950"

@@ -259,6 +259,54 @@ hipError_t scratch_for(int dev, hipStream_t stream, size_t need, void **out,
     return hipSuccess;
 }
 
+// A second per-stream buffer for work arrays whose contents do not outlive
+// a call (FusedMM's values, the element-balanced kernel's carry slots).  It
+// only grows; calls on one stream are ordered, so reusing it is safe.  Not
+// cleared (every call writes what it reads).
+struct StreamAux {
+    int dev;
+    hipStream_t stream;
+    void *ptr;
+    size_t size;
+};
+
+std::vector<StreamAux> g_aux;
+
+hipError_t aux_for(int dev, hipStream_t stream, size_t need, void **out)
+{
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    StreamAux *slot = nullptr;
+    for (StreamAux &e : g_aux)
+        if (e.dev == dev && e.stream == stream)
+            slot = &e;
+    if (slot && slot->size >= need) {
+        *out = slot->ptr;
+        return hipSuccess;
+    }
+    hipMemPool_t pool;
+    hipError_t err = pool_for_device(dev, &pool);
+    if (err != hipSuccess)
+        return err;
+    size_t size = need;
+    if (slot && size < slot->size + slot->size / 4)
+        size = slot->size + slot->size / 4;
+    void *ptr = nullptr;
+    err = hipMallocFromPoolAsync(&ptr, size, pool, stream);
+    if (err != hipSuccess)
+        return err;
+    if (ptr == nullptr)
+        return hipErrorOutOfMemory;
+    if (slot) {
+        hipFreeAsync(slot->ptr, stream);
+        slot->ptr = ptr;
+        slot->size = size;
+    } else {
+        g_aux.push_back(StreamAux{dev, stream, ptr, size});
+    }
+    *out = ptr;
+    return hipSuccess;
+}
+
 // --------------------------------------------------------------- timing
 
 // Kernel timing: the start/stop events are attached to the kernel dispatch
@@ -501,14 +549,11 @@ spmm_status_t run_fusedmm(const int32_t *rowptr, const int32_t *colind,
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess)
         return fail_hip(err, "hipGetDevice");
-    hipMemPool_t pool;
-    if ((err = pool_for_device(dev, &pool)) != hipSuccess)
-        return fail_hip(err, "memory pool");
     float *vals = nullptr;
     const size_t bytes = (size_t)(nnz > 0 ? nnz : 1) * sizeof(float);
     if (test_fail_alloc())
         return fail(SPMM_ERROR_OUT_OF_MEMORY, "allocation failure forced by SPMM_TEST_FAIL_ALLOC");
-    err = hipMallocFromPoolAsync((void **)&vals, bytes, pool, stream);
+    err = aux_for(dev, stream, bytes, (void **)&vals);
     if (err == hipErrorOutOfMemory)
         return fail(SPMM_ERROR_OUT_OF_MEMORY, "value scratch allocation failed");
     if (err != hipSuccess)
@@ -521,10 +566,8 @@ spmm_status_t run_fusedmm(const int32_t *rowptr, const int32_t *colind,
         timing = g_timing;
         if (timing &&
             ((err = take_event(&tc.work0)) != hipSuccess ||
-             (err = take_event(&tc.work1)) != hipSuccess)) {
-            hipFreeAsync(vals, stream);
+             (err = take_event(&tc.work1)) != hipSuccess))
             return fail_hip(err, "hipEventCreate");
-        }
     }
     spmm_status_t st = SPMM_SUCCESS;
     if (nnz > 0) {
@@ -546,7 +589,6 @@ spmm_status_t run_fusedmm(const int32_t *rowptr, const int32_t *colind,
         st = run_with(SPMM_DTYPE_F32, rowptr, colind, vals, D, E, M, K, N, nullptr,
                       stream_ptr, true, nnz > 0 ? nullptr : tc.work0, tc.work1,
                       true);
-    hipFreeAsync(vals, stream);
     if (st == SPMM_SUCCESS && timing) {
         std::lock_guard<std::mutex> lock(g_time_mu);
         g_timed.push_back(tc);
@@ -554,9 +596,79 @@ spmm_status_t run_fusedmm(const int32_t *rowptr, const int32_t *colind,
     return st;
 }
 
+// The element-balanced product: carry slots from the pool, two launches.
+spmm_status_t run_eb(int32_t dtype, const int32_t *rowptr, const int32_t *colind,
+                     const void *vals, const void *B, float *C, int64_t M,
+                     int64_t K, int64_t N, void *stream_ptr)
+{
+    g_last_error.clear();
+    spmm_status_t st = check_args(dtype, rowptr, B, C, M, K, N);
+    if (st != SPMM_SUCCESS)
+        return st;
+    if (M == 0 || N == 0)
+        return SPMM_SUCCESS;
+    if (test_fail_alloc())
+        return fail(SPMM_ERROR_OUT_OF_MEMORY, "allocation failure forced by SPMM_TEST_FAIL_ALLOC");
+    hipStream_t stream = (hipStream_t)stream_ptr;
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return fail_hip(err, "hipGetDevice");
+    const int64_t waves = eb_waves();
+    if (waves <= 0)
+        return fail(SPMM_ERROR_HIP, "device query failed");
+    const size_t row_bytes = align_up(8 * waves, 256);
+    const size_t bytes = row_bytes + (size_t)(2 * waves) * (size_t)N * sizeof(float);
+    char *mem = nullptr;
+    err = aux_for(dev, stream, bytes, (void **)&mem);
+    if (err == hipErrorOutOfMemory)
+        return fail(SPMM_ERROR_OUT_OF_MEMORY, "carry allocation failed");
+    if (err != hipSuccess)
+        return fail_hip(err, "carry allocation");
+    TimedCall tc{};
+    bool timing;
+    {
+        std::lock_guard<std::mutex> lock(g_time_mu);
+        timing = g_timing;
+        if (timing &&
+            ((err = take_event(&tc.work0)) != hipSuccess ||
+             (err = take_event(&tc.work1)) != hipSuccess))
+            return fail_hip(err, "hipEventCreate");
+    }
+    EbArgs a;
+    a.rowptr = rowptr;
+    a.colind = colind;
+    a.vals = vals;
+    a.B = B;
+    a.C = C;
+    a.M = M;
+    a.K = K;
+    a.N = N;
+    a.waves = waves;
+    a.carry_row = (int32_t *)mem;
+    a.carry_val = (float *)(mem + row_bytes);
+    const WorkerConfig cfg = choose_worker(dtype, N, B, C);
+    err = launch_eb(cfg, a, stream, tc.work0, tc.work1);
+    if (err != hipSuccess)
+        return fail_hip(err, "element-balanced kernel");
+    if (timing) {
+        std::lock_guard<std::mutex> lock(g_time_mu);
+        g_timed.push_back(tc);
+    }
+    return SPMM_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
+
+spmm_status_t spmm_csr_eb(int32_t dtype, const int32_t *rowptr,
+                          const int32_t *colind, const void *vals,
+                          const void *B, float *C, int64_t M, int64_t K,
+                          int64_t N, void *stream)
+{
+    return run_eb(dtype, rowptr, colind, vals, B, C, M, K, N, stream);
+}
 
 spmm_status_t fusedmm_csr_f32(const int32_t *rowptr, const int32_t *colind,
                               const float *C, const float *B, const float *D,

@@ -1,0 +1,310 @@
+// gather.h -- device building blocks shared by the product kernels: lane
+// groups and their column layout, exact loads of B vectors (fp32 or bf16),
+// the staged (column, value) entries, batches of U gathers issued without
+// branches, accumulation, row stores and the reduction across groups.
+// Included by worker.hip and eb.hip (each keeps its own copy: everything
+// here is in an anonymous namespace).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+#include "spmm.h"
+
+namespace sdl {
+namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Loads of VEC consecutive elements of B and their exact widening to fp32.
+// load() takes a flat address; load_buf() a byte offset into a buffer
+// resource covering B (used when B is below 4 GiB: one 32-bit offset per
+// gather instead of a 64-bit address).
+template <int DT, int VEC> struct BLoad;
+
+template <> struct BLoad<SPMM_DTYPE_F32, 4> {
+    typedef f32x4 raw;
+    static __device__ raw load(const void *p) { return *(const f32x4 *)p; }
+    static __device__ raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off)
+    { return __builtin_bit_cast(raw, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0)); }
+    static __device__ void widen(const raw &r, float (&o)[4])
+    { o[0] = r.x; o[1] = r.y; o[2] = r.z; o[3] = r.w; }
+};
+template <> struct BLoad<SPMM_DTYPE_F32, 2> {
+    typedef f32x2 raw;
+    static __device__ raw load(const void *p) { return *(const f32x2 *)p; }
+    static __device__ raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off)
+    { return __builtin_bit_cast(raw, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0)); }
+    static __device__ void widen(const raw &r, float (&o)[2])
+    { o[0] = r.x; o[1] = r.y; }
+};
+template <> struct BLoad<SPMM_DTYPE_F32, 1> {
+    typedef float raw;
+    static __device__ raw load(const void *p) { return *(const float *)p; }
+    static __device__ raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off)
+    { return __builtin_bit_cast(raw, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0)); }
+    static __device__ void widen(const raw &r, float (&o)[1]) { o[0] = r; }
+};
+template <> struct BLoad<SPMM_DTYPE_BF16, 8> {
+    typedef u32x4 raw;
+    static __device__ raw load(const void *p) { return *(const u32x4 *)p; }
+    static __device__ raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off)
+    { return __builtin_bit_cast(raw, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0)); }
+    static __device__ void widen(const raw &r, float (&o)[8])
+    {
+        o[0] = bf16_lo(r.x); o[1] = bf16_hi(r.x);
+        o[2] = bf16_lo(r.y); o[3] = bf16_hi(r.y);
+        o[4] = bf16_lo(r.z); o[5] = bf16_hi(r.z);
+        o[6] = bf16_lo(r.w); o[7] = bf16_hi(r.w);
+    }
+};
+template <> struct BLoad<SPMM_DTYPE_BF16, 4> {
+    typedef u32x2 raw;
+    static __device__ raw load(const void *p) { return *(const u32x2 *)p; }
+    static __device__ raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off)
+    { return __builtin_bit_cast(raw, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0)); }
+    static __device__ void widen(const raw &r, float (&o)[4])
+    {
+        o[0] = bf16_lo(r.x); o[1] = bf16_hi(r.x);
+        o[2] = bf16_lo(r.y); o[3] = bf16_hi(r.y);
+    }
+};
+template <> struct BLoad<SPMM_DTYPE_BF16, 2> {
+    typedef uint32_t raw;
+    static __device__ raw load(const void *p) { return *(const uint32_t *)p; }
+    static __device__ raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off)
+    { return __builtin_bit_cast(raw, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0)); }
+    static __device__ void widen(const raw &r, float (&o)[2])
+    { o[0] = bf16_lo(r); o[1] = bf16_hi(r); }
+};
+template <> struct BLoad<SPMM_DTYPE_BF16, 1> {
+    typedef uint16_t raw;
+    static __device__ raw load(const void *p) { return *(const uint16_t *)p; }
+    static __device__ raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off)
+    { return __builtin_bit_cast(raw, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0)); }
+    static __device__ void widen(const raw &r, float (&o)[1])
+    { o[0] = __uint_as_float((uint32_t)r << 16); }
+};
+
+template <int DT> struct ElemSize;
+template <> struct ElemSize<SPMM_DTYPE_F32> { static constexpr int v = 4; };
+template <> struct ElemSize<SPMM_DTYPE_BF16> { static constexpr int v = 2; };
+
+// Word 3 of a raw buffer resource on the gfx9 family (gfx950): 32-bit
+// elements, no swizzle; with stride 0 the record count is a byte count and
+// loads past it return zero.
+constexpr int kBufferWord3 = 0x00020000;
+
+// A stored entry as staged in LDS: column and value (already fp32).
+struct Entry {
+    int32_t col;
+    float val;
+};
+
+// Per-wavefront LDS staging area.  A short tile stages at most kShortCap
+// entries (the host sizes tiles so that T * short_max <= kShortCap); medium
+// rows and long chunks use the first 64 entries.
+constexpr int kStageSlots = kShortCap / kWave;  // staged entries per lane
+
+struct WaveStage {
+    Entry ent[kShortCap];
+    uint8_t rid[kShortCap];   // row of the entry within its tile
+};
+
+
+// Exclusive prefix sum of v over the 64 lanes of the wavefront.
+__device__ inline int wave_exclusive_sum(int v)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off)
+            x += y;
+    }
+    return x - v;
+}
+
+template <int DT> __device__ inline float load_val(const void *vals, int64_t p);
+template <> __device__ inline float load_val<SPMM_DTYPE_F32>(const void *vals, int64_t p)
+{ return ((const float *)vals)[p]; }
+template <> __device__ inline float load_val<SPMM_DTYPE_BF16>(const void *vals, int64_t p)
+{ return __uint_as_float((uint32_t)((const uint16_t *)vals)[p] << 16); }
+
+// Compile-time shape of one worker variant.
+template <int DT_, int VEC_, int G_, int NV_, bool BUF_>
+struct Shape {
+    static constexpr bool BUF = BUF_;   // B addressed through a buffer resource
+    static constexpr int DT = DT_;
+    static constexpr int VEC = VEC_;
+    static constexpr int G = G_;
+    static constexpr int NV = NV_;
+    static constexpr int R = kWave / G_;          // groups per wavefront
+    static constexpr int COLS = G_ * VEC_ * NV_;  // columns per column pass
+    static constexpr int U = NV_ == 1 ? 8 : (NV_ == 2 ? 4 : 2);  // gathers in flight
+    static constexpr int ESZ = ElemSize<DT_>::v;
+};
+
+// Byte offsets (within a row of B) of this lane's NV vectors for the column
+// pass starting at col0, and whether each lies inside the row.  Lanes past
+// the end of the row read the row's last full vector instead, so every load
+// has a valid address and none needs a branch.
+template <class S>
+struct LaneCols {
+    int64_t ofs[S::NV];
+    bool live[S::NV];
+};
+
+template <class S>
+__device__ inline LaneCols<S> lane_cols(int64_t N, int64_t col0, int j)
+{
+    LaneCols<S> lc;
+#pragma unroll
+    for (int k = 0; k < S::NV; ++k) {
+        const int64_t c = col0 + (int64_t)(k * S::G + j) * S::VEC;
+        lc.live[k] = c < N;
+        lc.ofs[k] = (c < N ? c : N - S::VEC) * S::ESZ;
+    }
+    return lc;
+}
+
+// Where B lives: a buffer resource (BUF) or a flat pointer.
+struct BSrc {
+    __amdgpu_buffer_rsrc_t rsrc;
+    const char *base;
+};
+
+// One batch of up to U gathers of a lane group: the raw B vectors and the
+// entry values.
+template <class S>
+struct Batch {
+    typename BLoad<S::DT, S::VEC>::raw buf[S::U][S::NV];
+    float v[S::U];
+};
+
+// Issue the gathers of entries st[q .. q+n) (1 <= n <= U) back to back, with
+// no branches: slots past n repeat entry q.  The caller masks those slots
+// when accumulating.
+template <class S>
+__device__ inline void issue(Batch<S> &bt, const Entry *st, int q, int n,
+                             const BSrc &src, uint32_t row_bytes,
+                             const LaneCols<S> &lc)
+{
+    typedef BLoad<S::DT, S::VEC> L;
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+        const Entry e = st[u < n ? q + u : q];
+        bt.v[u] = e.val;
+        if constexpr (S::BUF) {
+            const uint32_t row = (uint32_t)e.col * row_bytes;
+#pragma unroll
+            for (int k = 0; k < S::NV; ++k)
+                bt.buf[u][k] = L::load_buf(src.rsrc, row + (uint32_t)lc.ofs[k]);
+        } else {
+            const char *row = src.base + (uint64_t)(uint32_t)e.col * row_bytes;
+#pragma unroll
+            for (int k = 0; k < S::NV; ++k)
+                bt.buf[u][k] = L::load(row + lc.ofs[k]);
+        }
+    }
+}
+
+// acc += v[u] * B-vector[u] when `on`; otherwise acc is left as it was (a
+// select, not a branch, so the value of an unused slot never matters).
+template <class S>
+__device__ inline void accumulate(const Batch<S> &bt, int u, bool on,
+                                  float (&acc)[S::NV][S::VEC])
+{
+    typedef BLoad<S::DT, S::VEC> L;
+#pragma unroll
+    for (int k = 0; k < S::NV; ++k) {
+        float b[S::VEC];
+        L::widen(bt.buf[u][k], b);
+#pragma unroll
+        for (int x = 0; x < S::VEC; ++x) {
+            const float t = fmaf(bt.v[u], b[x], acc[k][x]);
+            acc[k][x] = on ? t : acc[k][x];
+        }
+    }
+}
+
+// Group-local SAXPY over cnt staged entries: acc += val * B[col, cols of lane].
+template <class S>
+__device__ inline void consume(const Entry *st, int cnt, const BSrc &src,
+                               uint32_t row_bytes, const LaneCols<S> &lc,
+                               float (&acc)[S::NV][S::VEC])
+{
+    for (int u = 0; u < cnt; u += S::U) {
+        const int n = cnt - u < S::U ? cnt - u : S::U;
+        Batch<S> bt;
+        issue<S>(bt, st, u, n, src, row_bytes, lc);
+#pragma unroll
+        for (int x = 0; x < S::U; ++x)
+            accumulate<S>(bt, x, x < n, acc);
+    }
+}
+
+template <class S>
+__device__ inline void zero_acc(float (&acc)[S::NV][S::VEC])
+{
+#pragma unroll
+    for (int k = 0; k < S::NV; ++k)
+#pragma unroll
+        for (int x = 0; x < S::VEC; ++x)
+            acc[k][x] = 0.0f;
+}
+
+// Store (or atomically add) this lane's columns of one C row.
+template <class S, bool ATOMIC>
+__device__ inline void emit_row(float *C, int64_t row, int64_t N, int64_t col0,
+                                int j, const float (&acc)[S::NV][S::VEC])
+{
+    float *crow = C + row * N + col0;
+#pragma unroll
+    for (int k = 0; k < S::NV; ++k) {
+        const int64_t c = (int64_t)(k * S::G + j) * S::VEC;
+        if (col0 + c >= N)
+            continue;
+        if constexpr (ATOMIC) {
+#pragma unroll
+            for (int x = 0; x < S::VEC; ++x)
+                unsafeAtomicAdd(crow + c + x, acc[k][x]);
+        } else if constexpr (S::VEC % 4 == 0) {
+#pragma unroll
+            for (int x = 0; x < S::VEC; x += 4) {
+                f32x4 w = {acc[k][x], acc[k][x + 1], acc[k][x + 2], acc[k][x + 3]};
+                *(f32x4 *)(crow + c + x) = w;
+            }
+        } else if constexpr (S::VEC == 2) {
+            f32x2 w = {acc[k][0], acc[k][1]};
+            *(f32x2 *)(crow + c) = w;
+        } else {
+            crow[c] = acc[k][0];
+        }
+    }
+}
+
+// Sum the partial rows of the R groups (butterfly over lane distance
+// G, 2G, ...).  Groups that received no entries hold zeros.
+template <class S>
+__device__ inline void reduce_groups(float (&acc)[S::NV][S::VEC])
+{
+#pragma unroll
+    for (int off = S::G; off < kWave; off <<= 1)
+#pragma unroll
+        for (int k = 0; k < S::NV; ++k)
+#pragma unroll
+            for (int x = 0; x < S::VEC; ++x)
+                acc[k][x] += __shfl_xor(acc[k][x], off);
+}
+
+}  // namespace
+}  // namespace sdl

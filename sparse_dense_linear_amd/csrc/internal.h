@@ -127,6 +127,28 @@ struct SddmmArgs {
 hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream,
                         hipEvent_t start, hipEvent_t stop);
 
+// One element-balanced product (eb.hip): equal spans of stored entries per
+// wavefront, partial rows at span ends combined through carry slots.
+struct EbArgs {
+    const int32_t *rowptr;
+    const int32_t *colind;
+    const void *vals;
+    const void *B;
+    float *C;
+    int64_t M;
+    int64_t K;
+    int64_t N;
+    int64_t waves;        // spans (wavefronts) of the launch
+    int32_t *carry_row;   // [2 * waves] row of each carry slot, -1 if unused
+    float *carry_val;     // [2 * waves * N] partial rows
+};
+
+// Enqueue the element-balanced kernel and its carry fix-up; start is
+// attached to the first launch, stop to the second.
+hipError_t launch_eb(const WorkerConfig &cfg, const EbArgs &a, hipStream_t stream,
+                     hipEvent_t start, hipEvent_t stop);
+int64_t eb_waves();
+
 // Plain descriptors for the plan export.
 struct LongRow {
     int32_t row;

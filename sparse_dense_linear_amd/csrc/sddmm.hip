@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
+#include "span.h"
 #include "spmm.h"
 
 namespace sdl {
@@ -79,27 +80,6 @@ struct SdShape {
     static_assert((kWave / R) % U == 0, "a batch is a whole number of steps");
 };
 
-// The row holding absolute position p: the last i in [0, M) with
-// rowptr[i] <= p (rowptr[0] <= p < rowptr[M] is required).  64-ary search:
-// each round narrows [lo, hi) to one of 64 equal parts.
-__device__ inline int64_t find_row(const int32_t *rowptr, int64_t M, int64_t p,
-                                   int lane)
-{
-    int64_t lo = 0, hi = M;  // rowptr[lo] <= p < rowptr[hi]
-    while (hi - lo > 1) {
-        const int64_t step = (hi - lo + kWave - 1) / kWave;
-        const int64_t idx = lo + lane * step;
-        const int64_t v = rowptr[idx < hi ? idx : hi - 1];
-        // the probes are in ascending order, so the lanes with v <= p form
-        // a prefix (lane 0 always: rowptr[lo] <= p)
-        const int c = __popcll(__ballot(idx < hi && v <= p));
-        const int64_t nlo = lo + (int64_t)(c - 1) * step;
-        hi = nlo + step < hi ? nlo + step : hi;
-        lo = nlo;
-    }
-    return lo;
-}
-
 template <class S>
 __global__ __launch_bounds__(kBlock) void sddmm_kernel(
     const int32_t *__restrict__ rowptr, const int32_t *__restrict__ colind,
@@ -130,26 +110,7 @@ __global__ __launch_bounds__(kBlock) void sddmm_kernel(
         const int64_t pe = base + (live ? e : s1 - 1);
         const int32_t col = colind[pe];
 
-        // Row of this lane's entry: the number of window values
-        // rowptr[i_cur + 1 + l] (l < 64) that are <= pe, added to i_cur.
-        int64_t row = 0;
-        bool done = false;
-        for (int64_t win = i_cur; !(__ballot(!done) == 0);) {
-            const int64_t wi = win + 1 + lane;
-            const int64_t wv = rowptr[wi < M ? wi : M];
-            int pos = 0;
-#pragma unroll
-            for (int st = kWave / 2; st > 0; st >>= 1)
-                if (__shfl(wv, pos + st - 1) <= pe)
-                    pos += st;
-            if (pos == kWave - 1 && __shfl(wv, kWave - 1) <= pe)
-                pos = kWave;
-            if (!done && pos < kWave) {
-                row = win + pos;
-                done = true;
-            }
-            win += kWave;
-        }
+        const int64_t row = row_in_window(rowptr, M, i_cur, pe, lane);
         i_cur = __shfl(row, kWave - 1);
 
         // The 64 dot products: group g takes entries k = u * R + g.
