@@ -44,27 +44,31 @@ struct EbStep {
     static constexpr int SU = S::R * UE;  // entries per step
 };
 
-// Zero rows [lo, hi) that hold no entries; group g takes every R-th empty
-// row found.
-template <class S>
-__device__ void zero_empty_rows(const EbArgs &a, int64_t lo, int64_t hi,
-                                int lane, int g, int j)
+// Zero rows [lo, hi) of C, the whole wavefront writing each row (rows of
+// N floats, lanes over the columns).
+__device__ void zero_rows(float *C, int64_t N, int64_t lo, int64_t hi, int lane)
 {
-    for (int64_t r0 = lo; r0 < hi; r0 += kWave) {
+    for (int64_t r = lo; r < hi; ++r)
+        for (int64_t c = lane; c < N; c += kWave)
+            C[r * N + c] = 0.0f;
+}
+
+// Zero the empty rows that follow row `last` and start at position p (no
+// entries, rowptr == p): the run of such rows, 64 at a time.
+__device__ void zero_empty_after(float *C, const int32_t *rowptr, int64_t M,
+                                 int64_t N, int64_t last, int64_t p, int lane)
+{
+    for (int64_t r0 = last + 1; r0 < M; r0 += kWave) {
         const int64_t r = r0 + lane;
-        const int64_t rc = r < hi ? r : hi - 1;  // rc + 1 <= hi <= M
-        const bool empty = r < hi && a.rowptr[rc + 1] == a.rowptr[rc];
-        uint64_t m = __ballot(empty);
-        for (int k = 0; m != 0; ++k) {
-            const int bit = __builtin_ctzll(m);
-            m &= m - 1;
-            if (k % S::R != g)
-                continue;
-            float z[S::NV][S::VEC];
-            zero_acc<S>(z);
-            for (int64_t col0 = 0; col0 < a.N; col0 += S::COLS)
-                emit_row<S, false>(a.C, r0 + bit, a.N, col0, j, z);
-        }
+        const int64_t rc = r < M ? r : M - 1;  // rc + 1 <= M
+        const bool empty_here = r < M && (int64_t)rowptr[rc] == p &&
+                                (int64_t)rowptr[rc + 1] == p;
+        // the empty rows at p form a prefix of the run
+        const uint64_t m = __ballot(empty_here);
+        const int cnt = __popcll(~m) == 0 ? kWave : __builtin_ctzll(~m);
+        zero_rows(C, N, r0, r0 + cnt, lane);
+        if (cnt < kWave)
+            break;
     }
 }
 
@@ -82,7 +86,8 @@ __device__ inline void from_group(const float (&src)[S::NV][S::VEC], int gg,
 }
 
 template <class S>
-__global__ __launch_bounds__(kBlock) void eb_kernel(EbArgs a)
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4)))
+void eb_kernel(EbArgs a)
 {
     __shared__ Entry ent[kWavesPerBlock][kWave];
     __shared__ int32_t erow[kWavesPerBlock][kWave];
@@ -102,22 +107,25 @@ __global__ __launch_bounds__(kBlock) void eb_kernel(EbArgs a)
     span = span < kWave ? kWave : span;
     const int64_t s0 = w * span < nnz ? w * span : nnz;
     const int64_t s1 = s0 + span < nnz ? s0 + span : nnz;
-    const int64_t last_wave = nnz == 0 ? 0 : (nnz - 1) / span;
 
     // carry slots 2w (head) and 2w+1 (tail): unused unless written below
     if (lane == 0) {
         a.carry_row[2 * w] = -1;
         a.carry_row[2 * w + 1] = -1;
     }
-    // empty rows starting in this span (the last span also takes those at
-    // position nnz, i.e. trailing empty rows)
-    if (w <= last_wave) {
-        const int64_t lo = w == 0 ? 0 : lower_row(rowptr, a.M, base + s0, lane);
-        const int64_t hi = w == last_wave ? a.M : lower_row(rowptr, a.M, base + s1, lane);
-        zero_empty_rows<S>(a, lo, hi, lane, g, j);
+    if (nnz == 0) {
+        // no entries at all: every row is a zero row
+        if (w == 0)
+            zero_rows(a.C, a.N, 0, a.M, lane);
+        return;
     }
     if (s0 >= s1)
         return;
+    // Empty rows are zeroed by one wavefront each: wavefront 0 takes those
+    // before the first stored entry, a span takes those between its own
+    // entries (found while walking) and those that start exactly at its end
+    // (after its last row, if that row ends there; the last span's are the
+    // trailing empty rows).
 
     const uint32_t row_bytes = (uint32_t)(a.N * S::ESZ);
     BSrc src;
@@ -128,8 +136,11 @@ __global__ __launch_bounds__(kBlock) void eb_kernel(EbArgs a)
             (int)(uint32_t)(a.K * a.N * S::ESZ), kBufferWord3);
     const int64_t r_first = find_row(rowptr, a.M, base + s0, lane);
     const bool first_partial = (int64_t)rowptr[r_first] < base + s0;
+    if (w == 0)
+        zero_rows(a.C, a.N, 0, r_first, lane);  // rows before the first entry
     Entry *st = ent[wid];
     int32_t *rw = erow[wid];
+    int64_t r_last = r_first;  // row of the span's last entry
 
     for (int64_t col0 = 0; col0 < a.N; col0 += S::COLS) {
         const LaneCols<S> lc = lane_cols<S>(a.N, col0, j);
@@ -153,14 +164,42 @@ __global__ __launch_bounds__(kBlock) void eb_kernel(EbArgs a)
             }
         };
 
+        // the first batch's entries and row window, loaded ahead
+        int64_t pe = base + (lane < s1 - s0 ? s0 + lane : s1 - 1);
+        int32_t ncol = a.colind[pe];
+        float nval = load_val<S::DT>(a.vals, pe);
+        int64_t nwin = rowptr[i_cur + 1 + lane < a.M ? i_cur + 1 + lane : a.M];
+        int64_t prev_last = r_first;  // row of the previous batch's last entry
+
         for (int64_t e0 = s0; e0 < s1; e0 += kWave) {
             const int nb = s1 - e0 < kWave ? (int)(s1 - e0) : kWave;
-            const int64_t pe = base + (lane < nb ? e0 + lane : s1 - 1);
             Entry en;
-            en.col = a.colind[pe];
-            en.val = load_val<S::DT>(a.vals, pe);
-            const int64_t row = row_in_window(rowptr, a.M, i_cur, pe, lane);
+            en.col = ncol;
+            en.val = nval;
+            const int64_t row = row_in_window(rowptr, a.M, i_cur, pe, lane, nwin);
             i_cur = __shfl(row, kWave - 1);
+            // the next batch's loads go out before this batch's gathers
+            const int64_t e1 = e0 + kWave;
+            if (e1 < s1) {
+                pe = base + (lane < s1 - e1 ? e1 + lane : s1 - 1);
+                ncol = a.colind[pe];
+                nval = load_val<S::DT>(a.vals, pe);
+                nwin = rowptr[i_cur + 1 + lane < a.M ? i_cur + 1 + lane : a.M];
+            }
+            if (col0 == 0) {
+                // rows skipped between consecutive entries have no entries
+                const int64_t before = lane == 0 ? prev_last : __shfl_up(row, 1);
+                const bool gap = lane < nb && row > before + 1;
+                uint64_t m = __ballot(gap);
+                while (m != 0) {
+                    const int l = __builtin_ctzll(m);
+                    m &= m - 1;
+                    const int64_t hi = __shfl(row, l);
+                    const int64_t lo = (l == 0 ? prev_last : __shfl(row, l - 1)) + 1;
+                    zero_rows(a.C, a.N, lo, hi, lane);
+                }
+            }
+            prev_last = i_cur;
             __builtin_amdgcn_wave_barrier();  // the previous batch is consumed
             st[lane] = en;
             rw[lane] = (int32_t)row;
@@ -253,6 +292,8 @@ __global__ __launch_bounds__(kBlock) void eb_kernel(EbArgs a)
             }
         }
 
+        r_last = i_cur;
+
         // The last open row: a tail carry if it goes on past the span.
         if ((int64_t)rowptr[open_row + 1] > base + s1) {
             if (open_row == r_first && first_partial) {
@@ -272,11 +313,16 @@ __global__ __launch_bounds__(kBlock) void eb_kernel(EbArgs a)
             flush_open();
         }
     }
+    // empty rows that start where this span ends (the last row ends there)
+    if ((int64_t)rowptr[r_last + 1] == base + s1)
+        zero_empty_after(a.C, rowptr, a.M, a.N, r_last, base + s1, lane);
 }
 
 // Rows split across spans: slot s starts a run if it holds a row and the
 // slot before it holds another; the run's slots are added in slot order and
-// the row is stored.  One wavefront per slot.
+// the row is stored.  One wavefront per slot: the run's end is found 64
+// slots per round (ballot), and the sum keeps 8 slot loads in flight while
+// adding them in order.
 __global__ __launch_bounds__(kBlock) void eb_fixup(const int32_t *carry_row,
                                                    const float *carry_val,
                                                    float *C, int64_t slots,
@@ -290,12 +336,30 @@ __global__ __launch_bounds__(kBlock) void eb_fixup(const int32_t *carry_row,
     if (r < 0 || (s > 0 && carry_row[s - 1] == r))
         return;
     int64_t e = s + 1;
-    while (e < slots && carry_row[e] == r)
-        ++e;
+    for (;;) {
+        const int64_t t = e + lane;
+        const bool same = t < slots && carry_row[t < slots ? t : slots - 1] == r;
+        const uint64_t stop = __ballot(!same);
+        if (stop != 0) {
+            e += __builtin_ctzll(stop);
+            break;
+        }
+        e += kWave;
+    }
+    constexpr int kAhead = 8;
     for (int64_t c = lane; c < N; c += kWave) {
         float v = 0.0f;
-        for (int64_t t = s; t < e; ++t)
-            v += carry_val[t * N + c];
+        for (int64_t t0 = s; t0 < e; t0 += kAhead) {
+            float x[kAhead];
+#pragma unroll
+            for (int u = 0; u < kAhead; ++u) {
+                const int64_t t = t0 + u < e ? t0 + u : e - 1;
+                x[u] = carry_val[t * N + c];
+            }
+#pragma unroll
+            for (int u = 0; u < kAhead; ++u)
+                v = t0 + u < e ? v + x[u] : v;
+        }
         C[(int64_t)r * N + c] = v;
     }
 }

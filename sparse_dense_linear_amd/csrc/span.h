@@ -61,13 +61,17 @@ __device__ inline int64_t lower_row(const int32_t *rowptr, int64_t M, int64_t p,
 // moves on by 64 rows while some lane's entry lies beyond it (runs of empty
 // rows).  Requires pe < rowptr[M].
 __device__ inline int64_t row_in_window(const int32_t *rowptr, int64_t M,
-                                        int64_t i_cur, int64_t pe, int lane)
+                                        int64_t i_cur, int64_t pe, int lane,
+                                        int64_t first_wv = -1)
 {
+    // first_wv: this lane's value of the first window, rowptr[min(i_cur + 1
+    // + lane, M)], when the caller has loaded it ahead (-1: load it here)
     int64_t row = 0;
     bool done = false;
     for (int64_t win = i_cur; __ballot(!done) != 0; win += kWave) {
         const int64_t wi = win + 1 + lane;
-        const int64_t wv = rowptr[wi < M ? wi : M];
+        const int64_t wv = (win == i_cur && first_wv >= 0) ? first_wv
+                                                           : (int64_t)rowptr[wi < M ? wi : M];
         int pos = 0;
 #pragma unroll
         for (int st = kWave / 2; st > 0; st >>= 1)
