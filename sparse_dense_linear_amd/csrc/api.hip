@@ -596,7 +596,8 @@ spmm_status_t run_fusedmm(const int32_t *rowptr, const int32_t *colind,
     return st;
 }
 
-// The element-balanced product: carry slots from the pool, two launches.
+// The element-balanced product: one launch; carry slots in the stream's
+// work buffer, arrival counters in its plan scratch.
 spmm_status_t run_eb(int32_t dtype, const int32_t *rowptr, const int32_t *colind,
                      const void *vals, const void *B, float *C, int64_t M,
                      int64_t K, int64_t N, void *stream_ptr)
@@ -617,8 +618,17 @@ spmm_status_t run_eb(int32_t dtype, const int32_t *rowptr, const int32_t *colind
     const int64_t waves = eb_waves();
     if (waves <= 0)
         return fail(SPMM_ERROR_HIP, "device query failed");
-    const size_t row_bytes = align_up(8 * waves, 256);
-    const size_t bytes = row_bytes + (size_t)(2 * waves) * (size_t)N * sizeof(float);
+    // arrival counters: the per-stream plan scratch (zeroed when created,
+    // one epoch per call), enough of it for one word per span
+    const ScratchLayout lay = scratch_layout(M > waves ? M : waves);
+    void *scratch = nullptr;
+    uint32_t epoch = 0;
+    err = scratch_for(dev, stream, (size_t)lay.total, &scratch, &epoch);
+    if (err == hipErrorOutOfMemory)
+        return fail(SPMM_ERROR_OUT_OF_MEMORY, "scratch allocation failed");
+    if (err != hipSuccess)
+        return fail_hip(err, "scratch allocation");
+    const size_t bytes = (size_t)(2 * waves) * (size_t)N * sizeof(float);
     char *mem = nullptr;
     err = aux_for(dev, stream, bytes, (void **)&mem);
     if (err == hipErrorOutOfMemory)
@@ -645,8 +655,9 @@ spmm_status_t run_eb(int32_t dtype, const int32_t *rowptr, const int32_t *colind
     a.K = K;
     a.N = N;
     a.waves = waves;
-    a.carry_row = (int32_t *)mem;
-    a.carry_val = (float *)(mem + row_bytes);
+    a.carry_val = (float *)mem;
+    a.arrive = carve((char *)scratch, lay).medium_rows;
+    a.epoch = epoch;
     const WorkerConfig cfg = choose_worker(dtype, N, B, C);
     err = launch_eb(cfg, a, stream, tc.work0, tc.work1);
     if (err != hipSuccess)

@@ -19,11 +19,14 @@
 //     wavefront's open row (a segmented reduction across the groups); a row
 //     that closes inside the span is stored;
 //   * the span's first row, if it started in an earlier span, and its last
-//     row, if it goes on past the span, are partial: they go to two carry
-//     slots per wavefront, and a second small kernel adds the carries of
-//     each row in slot order and stores the row;
-//   * the empty rows that start inside a span are written as zero rows by
-//     that span's wavefront.
+//     row, if it goes on past the span, are partial: each goes to a carry
+//     slot of the wavefront (device-coherent stores), and the wavefront
+//     then arrives on a counter of that row (tagged with the call's epoch);
+//     the arrival that completes the row's count adds the row's slots in
+//     span order and stores the row -- so the whole product is one launch;
+//   * empty rows are zeroed by one wavefront each (before the first entry:
+//     wavefront 0; between a span's entries: that span; starting exactly at
+//     a span's end: that span).
 // Every output element is the sum of its row's products in a fixed order,
 // so results repeat bit for bit.
 #include <hip/hip_ext.h>
@@ -31,6 +34,7 @@
 
 #include "gather.h"
 #include "internal.h"
+#include "plan_device.h"
 #include "span.h"
 #include "spmm.h"
 
@@ -72,6 +76,78 @@ __device__ void zero_empty_after(float *C, const int32_t *rowptr, int64_t M,
     }
 }
 
+// Store this lane's columns of a partial row into carry slot `slot` with
+// device-coherent stores (another XCD's wavefront may read it).
+template <class S>
+__device__ inline void store_partial(float *carry_val, int64_t slot, int64_t N,
+                                     int64_t col0, int j,
+                                     const float (&acc)[S::NV][S::VEC])
+{
+#pragma unroll
+    for (int k = 0; k < S::NV; ++k) {
+        const int64_t c = col0 + (int64_t)(k * S::G + j) * S::VEC;
+        if (c >= N)
+            continue;
+#pragma unroll
+        for (int x = 0; x < S::VEC; ++x)
+            __hip_atomic_store(carry_val + slot * N + c + x, acc[k][x],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Count one arrival on a counter tagged with the call's epoch (a word with
+// another tag counts as 0) and return the count including this arrival.
+// Lock-free: a retry happens only when another arrival got in first.
+__device__ inline uint32_t arrive(uint64_t *ctr, uint32_t epoch)
+{
+    uint64_t old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int tries = 0; tries < (1 << 20); ++tries) {
+        const uint32_t cnt = (uint32_t)(old >> 32) == epoch ? (uint32_t)old : 0u;
+        const uint64_t nw = ((uint64_t)epoch << 32) | (uint64_t)(cnt + 1);
+        if (__hip_atomic_compare_exchange_strong(ctr, &old, nw, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+            return cnt + 1;
+    }
+    return 0;  // not reached with the few arrivals a row has
+}
+
+// Row x was cut by span ends: its partials sit in the tail slot of the span
+// holding its first entry (wa) and in the head slots of spans wa+1 .. wb.
+// The wavefront whose arrival completes the count adds them in that order
+// (8 coherent loads in flight) and stores the row.
+__device__ void finish_split_row(const EbArgs &a, int64_t x, int64_t base,
+                                 int64_t span, int lane)
+{
+    const int64_t wa = ((int64_t)a.rowptr[x] - base) / span;
+    const int64_t wb = ((int64_t)a.rowptr[x + 1] - 1 - base) / span;
+    int c_arr = 0;
+    if (lane == 0)
+        c_arr = (int)arrive(a.arrive + wa, a.epoch);
+    c_arr = __shfl(c_arr, 0);
+    if (c_arr != (int)(wb - wa + 1))
+        return;
+    const int64_t n = wb - wa + 1;  // slots: 2wa+1, then 2(wa+1), ..., 2wb
+    constexpr int kAhead = 8;
+    for (int64_t c = lane; c < a.N; c += kWave) {
+        float v = 0.0f;
+        for (int64_t t0 = 0; t0 < n; t0 += kAhead) {
+            float xs[kAhead];
+#pragma unroll
+            for (int u = 0; u < kAhead; ++u) {
+                const int64_t t = t0 + u < n ? t0 + u : n - 1;
+                const int64_t slot = t == 0 ? 2 * wa + 1 : 2 * (wa + t);
+                xs[u] = __hip_atomic_load(a.carry_val + slot * a.N + c,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int u = 0; u < kAhead; ++u)
+                v = t0 + u < n ? v + xs[u] : v;
+        }
+        a.C[x * a.N + c] = v;
+    }
+}
+
 // Move group gg's slice of a partial row to every group (lane j of each
 // group gets lane j of group gg).
 template <class S>
@@ -108,11 +184,6 @@ void eb_kernel(EbArgs a)
     const int64_t s0 = w * span < nnz ? w * span : nnz;
     const int64_t s1 = s0 + span < nnz ? s0 + span : nnz;
 
-    // carry slots 2w (head) and 2w+1 (tail): unused unless written below
-    if (lane == 0) {
-        a.carry_row[2 * w] = -1;
-        a.carry_row[2 * w + 1] = -1;
-    }
     if (nnz == 0) {
         // no entries at all: every row is a zero row
         if (w == 0)
@@ -156,9 +227,7 @@ void eb_kernel(EbArgs a)
                 return;
             if (open_row == r_first && first_partial) {
                 if (g == 0)
-                    emit_row<S, false>(a.carry_val, 2 * w, a.N, col0, j, acc_open);
-                if (lane == 0)
-                    a.carry_row[2 * w] = (int32_t)open_row;
+                    store_partial<S>(a.carry_val, 2 * w, a.N, col0, j, acc_open);
             } else if (g == 0) {
                 emit_row<S, false>(a.C, open_row, a.N, col0, j, acc_open);
             }
@@ -294,74 +363,33 @@ void eb_kernel(EbArgs a)
 
         r_last = i_cur;
 
-        // The last open row: a tail carry if it goes on past the span.
+        // The last open row: if it goes on past the span it is partial (the
+        // head slot if it is also the span's first, partial row -- the whole
+        // span lies inside it -- else the tail slot).
         if ((int64_t)rowptr[open_row + 1] > base + s1) {
-            if (open_row == r_first && first_partial) {
-                // the whole span lies inside one row: the partial is the head
-                // carry, and a zero tail carry keeps the row's slots adjacent
+            if (open_row == r_first && first_partial)
                 flush_open();
-                float z[S::NV][S::VEC];
-                zero_acc<S>(z);
-                if (g == 0)
-                    emit_row<S, false>(a.carry_val, 2 * w + 1, a.N, col0, j, z);
-            } else if (g == 0) {
-                emit_row<S, false>(a.carry_val, 2 * w + 1, a.N, col0, j, acc_open);
-            }
-            if (lane == 0)
-                a.carry_row[2 * w + 1] = (int32_t)open_row;
+            else if (g == 0)
+                store_partial<S>(a.carry_val, 2 * w + 1, a.N, col0, j, acc_open);
         } else {
             flush_open();
         }
     }
+
+    // Rows cut by this span's ends: arrive once per row; the last arrival
+    // adds the row's partials and stores it.
+    const bool tail_split = (int64_t)rowptr[r_last + 1] > base + s1 &&
+                            !(r_last == r_first && first_partial);
+    if (first_partial || tail_split) {
+        wait_stores_done();  // the partials are visible device-wide first
+        if (first_partial)
+            finish_split_row(a, r_first, base, span, lane);
+        if (tail_split)
+            finish_split_row(a, r_last, base, span, lane);
+    }
     // empty rows that start where this span ends (the last row ends there)
     if ((int64_t)rowptr[r_last + 1] == base + s1)
         zero_empty_after(a.C, rowptr, a.M, a.N, r_last, base + s1, lane);
-}
-
-// Rows split across spans: slot s starts a run if it holds a row and the
-// slot before it holds another; the run's slots are added in slot order and
-// the row is stored.  One wavefront per slot: the run's end is found 64
-// slots per round (ballot), and the sum keeps 8 slot loads in flight while
-// adding them in order.
-__global__ __launch_bounds__(kBlock) void eb_fixup(const int32_t *carry_row,
-                                                   const float *carry_val,
-                                                   float *C, int64_t slots,
-                                                   int64_t N)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t s = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-    if (s >= slots)
-        return;
-    const int32_t r = carry_row[s];
-    if (r < 0 || (s > 0 && carry_row[s - 1] == r))
-        return;
-    int64_t e = s + 1;
-    for (;;) {
-        const int64_t t = e + lane;
-        const bool same = t < slots && carry_row[t < slots ? t : slots - 1] == r;
-        const uint64_t stop = __ballot(!same);
-        if (stop != 0) {
-            e += __builtin_ctzll(stop);
-            break;
-        }
-        e += kWave;
-    }
-    constexpr int kAhead = 8;
-    for (int64_t c = lane; c < N; c += kWave) {
-        float v = 0.0f;
-        for (int64_t t0 = s; t0 < e; t0 += kAhead) {
-            float x[kAhead];
-#pragma unroll
-            for (int u = 0; u < kAhead; ++u) {
-                const int64_t t = t0 + u < e ? t0 + u : e - 1;
-                x[u] = carry_val[t * N + c];
-            }
-#pragma unroll
-            for (int u = 0; u < kAhead; ++u)
-                v = t0 + u < e ? v + x[u] : v;
-        }
-        C[(int64_t)r * N + c] = v;
-    }
 }
 
 template <class S>
@@ -371,14 +399,7 @@ hipError_t launch_eb_shape(const EbArgs &a0, hipStream_t stream, hipEvent_t e0,
     EbArgs a = a0;
     const int64_t blocks = (a.waves + kWavesPerBlock - 1) / kWavesPerBlock;
     hipExtLaunchKernelGGL(eb_kernel<S>, dim3((unsigned)blocks), dim3(kBlock), 0,
-                          stream, e0, nullptr, 0, a);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess)
-        return err;
-    const int64_t slots = 2 * a.waves;
-    const int64_t fblocks = (slots + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipExtLaunchKernelGGL(eb_fixup, dim3((unsigned)fblocks), dim3(kBlock), 0, stream,
-                          nullptr, e1, 0, a.carry_row, a.carry_val, a.C, slots, a.N);
+                          stream, e0, e1, 0, a);
     return hipGetLastError();
 }
 

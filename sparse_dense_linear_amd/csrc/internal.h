@@ -139,12 +139,12 @@ struct EbArgs {
     int64_t K;
     int64_t N;
     int64_t waves;        // spans (wavefronts) of the launch
-    int32_t *carry_row;   // [2 * waves] row of each carry slot, -1 if unused
-    float *carry_val;     // [2 * waves * N] partial rows
+    float *carry_val;     // [2 * waves * N] partial rows: head and tail slot
+    uint64_t *arrive;     // [waves] arrival counters, tagged with epoch
+    uint32_t epoch;       // this call's epoch (words with another tag are 0)
 };
 
-// Enqueue the element-balanced kernel and its carry fix-up; start is
-// attached to the first launch, stop to the second.
+// Enqueue the element-balanced kernel (one launch; start/stop attached).
 hipError_t launch_eb(const WorkerConfig &cfg, const EbArgs &a, hipStream_t stream,
                      hipEvent_t start, hipEvent_t stop);
 int64_t eb_waves();
