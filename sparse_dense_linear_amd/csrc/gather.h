@@ -252,6 +252,47 @@ __device__ inline void consume(const Entry *st, int cnt, const BSrc &src,
     }
 }
 
+// As issue(), with entry k held in lane k's (col, val) instead of LDS.
+template <class S>
+__device__ inline void issue_lanes(Batch<S> &bt, int32_t col, float val, int q, int n,
+                                   const BSrc &src, uint32_t row_bytes,
+                                   const LaneCols<S> &lc)
+{
+    typedef BLoad<S::DT, S::VEC> L;
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+        const int from = u < n ? q + u : q;
+        const int32_t c = __shfl(col, from);
+        bt.v[u] = __shfl(val, from);
+        if constexpr (S::BUF) {
+            const uint32_t row = (uint32_t)c * row_bytes;
+#pragma unroll
+            for (int k = 0; k < S::NV; ++k)
+                bt.buf[u][k] = L::load_buf(src.rsrc, row + (uint32_t)lc.ofs[k]);
+        } else {
+            const char *row = src.base + (uint64_t)(uint32_t)c * row_bytes;
+#pragma unroll
+            for (int k = 0; k < S::NV; ++k)
+                bt.buf[u][k] = L::load(row + lc.ofs[k]);
+        }
+    }
+}
+
+template <class S>
+__device__ inline void consume_lanes(int32_t col, float val, int first, int cnt,
+                                     const BSrc &src, uint32_t row_bytes,
+                                     const LaneCols<S> &lc, float (&acc)[S::NV][S::VEC])
+{
+    for (int u = 0; u < cnt; u += S::U) {
+        const int n = cnt - u < S::U ? cnt - u : S::U;
+        Batch<S> bt;
+        issue_lanes<S>(bt, col, val, first + u, n, src, row_bytes, lc);
+#pragma unroll
+        for (int x = 0; x < S::U; ++x)
+            accumulate<S>(bt, x, x < n, acc);
+    }
+}
+
 template <class S>
 __device__ inline void zero_acc(float (&acc)[S::NV][S::VEC])
 {

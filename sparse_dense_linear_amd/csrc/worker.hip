@@ -56,14 +56,15 @@ namespace sdl {
 namespace {
 
 // One wavefront accumulates positions [p0, p1) (p1 > p0) of one row: 64-entry
-// chunks of colind/vals are loaded coalesced (the next one prefetched into
-// registers while the current one is consumed) and staged in LDS; group g
-// consumes entries g*G .. g*G+G-1 of each chunk.
+// chunks of colind/vals are loaded coalesced, one entry per lane (the next
+// chunk prefetched into registers while the current one is consumed), and
+// group g consumes entries g*G .. g*G+G-1 of each chunk, reading them from
+// the lanes that hold them.
 template <class S>
-__device__ inline void wave_range(const WorkerArgs &a, Entry *st, int lane,
-                                  int g, int64_t p0, int64_t p1,
-                                  const BSrc &src, const LaneCols<S> &lc,
-                                  uint32_t row_bytes, float (&acc)[S::NV][S::VEC])
+__device__ inline void wave_range(const WorkerArgs &a, int lane, int g,
+                                  int64_t p0, int64_t p1, const BSrc &src,
+                                  const LaneCols<S> &lc, uint32_t row_bytes,
+                                  float (&acc)[S::NV][S::VEC])
 {
     zero_acc<S>(acc);
     // positions past the range read the range's last entry (valid address)
@@ -72,16 +73,8 @@ __device__ inline void wave_range(const WorkerArgs &a, Entry *st, int lane,
     float nvv = load_val<S::DT>(a.vals, p);
     for (int64_t base = p0; base < p1; base += kWave) {
         const int n = p1 - base < kWave ? (int)(p1 - base) : kWave;
-        // LDS hand-offs between the lanes of one wavefront need no barrier:
-        // its LDS operations execute in program order, and the compiler
-        // keeps stores and loads with data-dependent indices in order.  (An
-        // explicit wave barrier here costs about 2 % of the call.)
-        if (lane < n) {
-            Entry e;
-            e.col = nc;
-            e.val = nvv;
-            st[lane] = e;
-        }
+        const int32_t col = nc;
+        const float val = nvv;
         const int64_t nb = base + kWave;
         if (nb < p1) {
             p = nb + lane < p1 ? nb + lane : p1 - 1;
@@ -90,7 +83,7 @@ __device__ inline void wave_range(const WorkerArgs &a, Entry *st, int lane,
         }
         int cnt = n - g * S::G;
         cnt = cnt < 0 ? 0 : (cnt > S::G ? S::G : cnt);
-        consume<S>(st + g * S::G, cnt, src, row_bytes, lc, acc);
+        consume_lanes<S>(col, val, g * S::G, cnt, src, row_bytes, lc, acc);
     }
 }
 
@@ -147,14 +140,14 @@ __device__ inline bool medium_ready(const WorkerArgs &a, int64_t i, int64_t *row
 // One wavefront accumulates row `row` over positions [p0, p1) and stores
 // (medium row) or atomically adds (long-row chunk) the result.
 template <class S, bool ATOMIC>
-__device__ void do_range(const WorkerArgs &a, WaveStage &ws, int lane, int g,
-                         int j, int64_t row, int64_t p0, int64_t p1,
+__device__ void do_range(const WorkerArgs &a, int lane, int g, int j,
+                         int64_t row, int64_t p0, int64_t p1,
                          const BSrc &src, uint32_t row_bytes)
 {
     for (int64_t col0 = 0; col0 < a.N; col0 += S::COLS) {
         const LaneCols<S> lc = lane_cols<S>(a.N, col0, j);
         float acc[S::NV][S::VEC];
-        wave_range<S>(a, ws.ent, lane, g, p0, p1, src, lc, row_bytes, acc);
+        wave_range<S>(a, lane, g, p0, p1, src, lc, row_bytes, acc);
         reduce_groups<S>(acc);
         if (g == 0)
             emit_row<S, ATOMIC>(a.C, row, a.N, col0, j, acc);
@@ -208,6 +201,8 @@ __device__ void do_short_tile(const WorkerArgs &a, WaveStage &ws, int lane,
             srow[i] = l;
         }
     }
+    // every lane has read the previous tile's entries
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int i = 0; i < kStageSlots; ++i) {
         const int e = i * kWave + lane;
@@ -219,7 +214,8 @@ __device__ void do_short_tile(const WorkerArgs &a, WaveStage &ws, int lane,
             ws.rid[e] = (uint8_t)srow[i];
         }
     }
-    // (staged before any lane reads it: see wave_range on LDS ordering)
+    // the tile is staged before any lane reads it
+    __builtin_amdgcn_wave_barrier();
 
     const int first = g * P;
     const int beg = __shfl(off, first);
@@ -335,12 +331,12 @@ __device__ inline void do_item(const WorkerArgs &a, const ProductShape &ps,
         // chunk was published; the atomic adds address it through the
         // published row, so they come after the clearing.
         if (wait_for([&]() { return chunk_ready(a, d, n_long, &row, &p0, &p1); }))
-            do_range<S, true>(a, ws, lane, g, j, row, p0, p1, src, row_bytes);
+            do_range<S, true>(a, lane, g, j, row, p0, p1, src, row_bytes);
         else
             note_fault(a, lane);
     } else if (d < n_ch + n_med) {
         if (wait_for([&]() { return medium_ready(a, d - n_ch, &row); }))
-            do_range<S, false>(a, ws, lane, g, j, row, a.rowptr[row],
+            do_range<S, false>(a, lane, g, j, row, a.rowptr[row],
                                a.rowptr[row + 1], src, row_bytes);
         else
             note_fault(a, lane);
