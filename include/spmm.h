@@ -231,12 +231,17 @@ spmm_status_t sddmm_csr_bf16in_f32acc(const int32_t *rowptr,
  *   nnz = rowptr[M] - rowptr[0] (a precondition).
  * E is overwritten; rows with no stored entries become zero rows.
  *
- * Two launches on `stream`: the SDDMM values are written to a scratch array
- * of nnz floats (kept per stream by the library, from its stream-ordered
- * pool, grown when a call needs more), and the sparse x dense product reads
- * them as the values of A with D as its dense operand.  Errors and ownership as for the
- * product; SPMM_ERROR_OUT_OF_MEMORY if the scratch array cannot be had.
- * Numerics: each value is rounded to fp32 before it weights D_j.
+ * One launch on `stream` when N is a multiple of 4 and at most 1024 and C,
+ * B, D and E are 16-byte aligned: the product's kernel (same plan, same
+ * per-stream scratch) forms each entry's value from C_i and B_j where the
+ * value is used, and no value array is written.  Otherwise two launches:
+ * the SDDMM values are written to a scratch array of nnz floats (kept per
+ * stream by the library, from its stream-ordered pool, grown when a call
+ * needs more), and the product reads them as the values of A with D as its
+ * dense operand.  Errors and ownership as for the product;
+ * SPMM_ERROR_OUT_OF_MEMORY if the scratch array cannot be had.
+ * Numerics: each value is rounded to fp32 before it weights D_j; both
+ * routes form it in the same order when they use the same lane-group width.
  */
 spmm_status_t fusedmm_csr_f32(const int32_t *rowptr, const int32_t *colind,
                               const float *C, const float *B, const float *D,

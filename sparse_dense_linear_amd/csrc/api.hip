@@ -369,7 +369,9 @@ spmm_status_t run_with(int32_t dtype, const int32_t *rowptr,
                        float *C, int64_t M, int64_t K, int64_t N,
                        const spmm_tuning_t *tuning, void *stream_ptr,
                        bool own_events, hipEvent_t e0, hipEvent_t e1,
-                       bool vals_relative = false)
+                       bool vals_relative = false,
+                       const float *dot_rows = nullptr,
+                       const float *dot_cols = nullptr)
 {
     spmm_status_t st = check_args(dtype, rowptr, B, C, M, K, N);
     if (st != SPMM_SUCCESS)
@@ -418,6 +420,8 @@ spmm_status_t run_with(int32_t dtype, const int32_t *rowptr,
     wa.vals_relative = vals_relative ? 1 : 0;
     wa.B = B;
     wa.C = C;
+    wa.dot_rows = dot_rows;
+    wa.dot_cols = dot_cols;
     wa.M = M;
     wa.K = K;
     wa.N = N;
@@ -544,6 +548,15 @@ spmm_status_t run_fusedmm(const int32_t *rowptr, const int32_t *colind,
         return fail(SPMM_ERROR_INVALID_VALUE, "null pointer");
     if ((((uintptr_t)C) | ((uintptr_t)B) | ((uintptr_t)D) | ((uintptr_t)E)) % 4 != 0)
         return fail(SPMM_ERROR_INVALID_VALUE, "operand not aligned to its element size");
+    // One launch when the FusedMM form of the worker covers the shape (fp32
+    // rows of at most one column pass, C and B aligned like D): each entry's
+    // value is formed where it is used and never stored.
+    const WorkerConfig cfg = choose_worker(SPMM_DTYPE_F32, N, D, E);
+    if (nnz > 0 && fused_fits(cfg, N) && ((uintptr_t)C) % 16 == 0 &&
+        ((uintptr_t)B) % 16 == 0)
+        return run_with(SPMM_DTYPE_F32, rowptr, colind, nullptr, D, E, M, K, N,
+                        nullptr, stream_ptr, false, nullptr, nullptr, false, C, B);
+    // Otherwise two launches: SDDMM into a value array, then the product.
     hipStream_t stream = (hipStream_t)stream_ptr;
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);

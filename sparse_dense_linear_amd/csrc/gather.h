@@ -139,17 +139,21 @@ template <> __device__ inline float load_val<SPMM_DTYPE_F32>(const void *vals, i
 template <> __device__ inline float load_val<SPMM_DTYPE_BF16>(const void *vals, int64_t p)
 { return __uint_as_float((uint32_t)((const uint16_t *)vals)[p] << 16); }
 
-// Compile-time shape of one worker variant.
-template <int DT_, int VEC_, int G_, int NV_, bool BUF_>
+// Compile-time shape of one worker variant.  FUSED: the FusedMM variant,
+// whose entry values are computed on the fly (two gathers per entry, so
+// half as many entries in flight).
+template <int DT_, int VEC_, int G_, int NV_, bool BUF_, bool FUSED_ = false>
 struct Shape {
     static constexpr bool BUF = BUF_;   // B addressed through a buffer resource
+    static constexpr bool FUSED = FUSED_;
     static constexpr int DT = DT_;
     static constexpr int VEC = VEC_;
     static constexpr int G = G_;
     static constexpr int NV = NV_;
     static constexpr int R = kWave / G_;          // groups per wavefront
     static constexpr int COLS = G_ * VEC_ * NV_;  // columns per column pass
-    static constexpr int U = NV_ == 1 ? 8 : (NV_ == 2 ? 4 : 2);  // gathers in flight
+    static constexpr int U0 = NV_ == 1 ? 8 : (NV_ == 2 ? 4 : 2);
+    static constexpr int U = FUSED_ ? (U0 / 2 > 1 ? U0 / 2 : 1) : U0;  // entries in flight
     static constexpr int ESZ = ElemSize<DT_>::v;
 };
 
@@ -190,6 +194,19 @@ struct Batch {
     float v[S::U];
 };
 
+// Vector k of this lane's columns of row `row` of a K x N operand.
+template <class S>
+__device__ inline typename BLoad<S::DT, S::VEC>::raw
+load_row_vec(const BSrc &src, int32_t row, uint32_t row_bytes,
+             const LaneCols<S> &lc, int k)
+{
+    typedef BLoad<S::DT, S::VEC> L;
+    if constexpr (S::BUF)
+        return L::load_buf(src.rsrc, (uint32_t)row * row_bytes + (uint32_t)lc.ofs[k]);
+    else
+        return L::load(src.base + (uint64_t)(uint32_t)row * row_bytes + lc.ofs[k]);
+}
+
 // Issue the gathers of entries st[q .. q+n) (1 <= n <= U) back to back, with
 // no branches: slots past n repeat entry q.  The caller masks those slots
 // when accumulating.
@@ -198,42 +215,40 @@ __device__ inline void issue(Batch<S> &bt, const Entry *st, int q, int n,
                              const BSrc &src, uint32_t row_bytes,
                              const LaneCols<S> &lc)
 {
-    typedef BLoad<S::DT, S::VEC> L;
 #pragma unroll
     for (int u = 0; u < S::U; ++u) {
         const Entry e = st[u < n ? q + u : q];
         bt.v[u] = e.val;
-        if constexpr (S::BUF) {
-            const uint32_t row = (uint32_t)e.col * row_bytes;
 #pragma unroll
-            for (int k = 0; k < S::NV; ++k)
-                bt.buf[u][k] = L::load_buf(src.rsrc, row + (uint32_t)lc.ofs[k]);
-        } else {
-            const char *row = src.base + (uint64_t)(uint32_t)e.col * row_bytes;
-#pragma unroll
-            for (int k = 0; k < S::NV; ++k)
-                bt.buf[u][k] = L::load(row + lc.ofs[k]);
-        }
+        for (int k = 0; k < S::NV; ++k)
+            bt.buf[u][k] = load_row_vec<S>(src, e.col, row_bytes, lc, k);
     }
 }
 
-// acc += v[u] * B-vector[u] when `on`; otherwise acc is left as it was (a
-// select, not a branch, so the value of an unused slot never matters).
+// acc += v * B-vector when `on`; otherwise acc is left as it was (a select,
+// not a branch, so the value of an unused slot never matters).
 template <class S>
-__device__ inline void accumulate(const Batch<S> &bt, int u, bool on,
-                                  float (&acc)[S::NV][S::VEC])
+__device__ inline void axpy(const typename BLoad<S::DT, S::VEC>::raw (&buf)[S::NV],
+                            float v, bool on, float (&acc)[S::NV][S::VEC])
 {
     typedef BLoad<S::DT, S::VEC> L;
 #pragma unroll
     for (int k = 0; k < S::NV; ++k) {
         float b[S::VEC];
-        L::widen(bt.buf[u][k], b);
+        L::widen(buf[k], b);
 #pragma unroll
         for (int x = 0; x < S::VEC; ++x) {
-            const float t = fmaf(bt.v[u], b[x], acc[k][x]);
+            const float t = fmaf(v, b[x], acc[k][x]);
             acc[k][x] = on ? t : acc[k][x];
         }
     }
+}
+
+template <class S>
+__device__ inline void accumulate(const Batch<S> &bt, int u, bool on,
+                                  float (&acc)[S::NV][S::VEC])
+{
+    axpy<S>(bt.buf[u], bt.v[u], on, acc);
 }
 
 // Group-local SAXPY over cnt staged entries: acc += val * B[col, cols of lane].
@@ -252,44 +267,103 @@ __device__ inline void consume(const Entry *st, int cnt, const BSrc &src,
     }
 }
 
-// As issue(), with entry k held in lane k's (col, val) instead of LDS.
-template <class S>
-__device__ inline void issue_lanes(Batch<S> &bt, int32_t col, float val, int q, int n,
-                                   const BSrc &src, uint32_t row_bytes,
-                                   const LaneCols<S> &lc)
-{
-    typedef BLoad<S::DT, S::VEC> L;
-#pragma unroll
-    for (int u = 0; u < S::U; ++u) {
-        const int from = u < n ? q + u : q;
-        const int32_t c = __shfl(col, from);
-        bt.v[u] = __shfl(val, from);
-        if constexpr (S::BUF) {
-            const uint32_t row = (uint32_t)c * row_bytes;
-#pragma unroll
-            for (int k = 0; k < S::NV; ++k)
-                bt.buf[u][k] = L::load_buf(src.rsrc, row + (uint32_t)lc.ofs[k]);
-        } else {
-            const char *row = src.base + (uint64_t)(uint32_t)c * row_bytes;
-#pragma unroll
-            for (int k = 0; k < S::NV; ++k)
-                bt.buf[u][k] = L::load(row + lc.ofs[k]);
-        }
-    }
-}
-
+// As consume(), with entry k held in lane k's (col, val) instead of LDS
+// (read by lane shuffles).
 template <class S>
 __device__ inline void consume_lanes(int32_t col, float val, int first, int cnt,
                                      const BSrc &src, uint32_t row_bytes,
                                      const LaneCols<S> &lc, float (&acc)[S::NV][S::VEC])
 {
-    for (int u = 0; u < cnt; u += S::U) {
-        const int n = cnt - u < S::U ? cnt - u : S::U;
+    for (int u0 = 0; u0 < cnt; u0 += S::U) {
+        const int n = cnt - u0 < S::U ? cnt - u0 : S::U;
         Batch<S> bt;
-        issue_lanes<S>(bt, col, val, first + u, n, src, row_bytes, lc);
+#pragma unroll
+        for (int u = 0; u < S::U; ++u) {
+            const int from = first + (u < n ? u0 + u : u0);
+            const int32_t c = __shfl(col, from);
+            bt.v[u] = __shfl(val, from);
+#pragma unroll
+            for (int k = 0; k < S::NV; ++k)
+                bt.buf[u][k] = load_row_vec<S>(src, c, row_bytes, lc, k);
+        }
 #pragma unroll
         for (int x = 0; x < S::U; ++x)
             accumulate<S>(bt, x, x < n, acc);
+    }
+}
+
+// FusedMM.  The value of an entry of row i at column j is <X_i, Y_j> (X the
+// M x N row operand, Y the K x N column operand), formed by the lane group
+// that holds the whole row (one column pass): each lane sums its vectors in
+// order (a chain of fused multiply-adds per vector, vectors past the end of
+// the row left out), then a butterfly over the group's G lanes adds the
+// parts.  This is the SDDMM kernel's order when the two use the same group
+// width, so the value is the SDDMM value bit for bit.
+template <class S>
+__device__ inline float group_dot(const float (&x)[S::NV][S::VEC],
+                                  const typename BLoad<S::DT, S::VEC>::raw (&y)[S::NV],
+                                  const LaneCols<S> &lc)
+{
+    typedef BLoad<S::DT, S::VEC> L;
+    float d = 0.0f;
+#pragma unroll
+    for (int k = 0; k < S::NV; ++k) {
+        float yv[S::VEC];
+        L::widen(y[k], yv);
+        float dk = 0.0f;
+#pragma unroll
+        for (int e = 0; e < S::VEC; ++e)
+            dk = fmaf(x[k][e], yv[e], dk);
+        d += lc.live[k] ? dk : 0.0f;
+    }
+#pragma unroll
+    for (int off = 1; off < S::G; off <<= 1)
+        d += __shfl_xor(d, off);
+    return d;
+}
+
+// This lane's columns of row `row` of the M x N row operand (flat address).
+template <class S>
+__device__ inline void load_x_row(const char *X, int64_t row, uint32_t row_bytes,
+                                  const LaneCols<S> &lc, float (&x)[S::NV][S::VEC])
+{
+    typedef BLoad<S::DT, S::VEC> L;
+#pragma unroll
+    for (int k = 0; k < S::NV; ++k)
+        L::widen(L::load(X + (uint64_t)row * row_bytes + lc.ofs[k]), x[k]);
+}
+
+// FusedMM over entries first .. first+cnt-1 of a chunk held one per lane
+// (column in lane k's `col`), all in the row whose X slice this lane holds:
+// acc += <X_i, Y_j> * D_j.  Both gathers of a batch are issued before any
+// value is formed.
+template <class S>
+__device__ inline void consume_lanes_fused(int32_t col, int first, int cnt,
+                                           const BSrc &dsrc, const BSrc &ysrc,
+                                           uint32_t row_bytes, const LaneCols<S> &lc,
+                                           const float (&x)[S::NV][S::VEC],
+                                           float (&acc)[S::NV][S::VEC])
+{
+    typedef typename BLoad<S::DT, S::VEC>::raw Raw;
+    for (int u0 = 0; u0 < cnt; u0 += S::U) {
+        const int n = cnt - u0 < S::U ? cnt - u0 : S::U;
+        int32_t c[S::U];
+        Raw yb[S::U][S::NV], db[S::U][S::NV];
+#pragma unroll
+        for (int u = 0; u < S::U; ++u) {
+            c[u] = __shfl(col, first + (u < n ? u0 + u : u0));
+#pragma unroll
+            for (int k = 0; k < S::NV; ++k)
+                yb[u][k] = load_row_vec<S>(ysrc, c[u], row_bytes, lc, k);
+        }
+#pragma unroll
+        for (int u = 0; u < S::U; ++u)
+#pragma unroll
+            for (int k = 0; k < S::NV; ++k)
+                db[u][k] = load_row_vec<S>(dsrc, c[u], row_bytes, lc, k);
+#pragma unroll
+        for (int u = 0; u < S::U; ++u)
+            axpy<S>(db[u], group_dot<S>(x, yb[u], lc), u < n, acc);
     }
 }
 

@@ -87,13 +87,22 @@ struct WorkerConfig {
 
 WorkerConfig choose_worker(int dtype, int64_t N, const void *B, const float *C);
 
+// Whether the FusedMM form of the worker covers cfg and N: fp32, 16-byte
+// vectors, and a whole row of N columns in one column pass.
+bool fused_fits(const WorkerConfig &cfg, int64_t N);
+
 struct WorkerArgs {
     const int32_t *rowptr;
     const int32_t *colind;
     const void *vals;      // value of entry p at vals[p] (or vals[p - rowptr[0]])
     int32_t vals_relative; // 1: vals is indexed from rowptr[0], not from 0
-    const void *B;
+    const void *B;         // FusedMM: D, the rows that the values weight
     float *C;              // null: plan only (no product)
+    // FusedMM only (null otherwise): the value of an entry of row i at
+    // column j is <dot_rows_i, dot_cols_j>, both fp32 with N columns
+    // (dot_rows M x N, dot_cols K x N), and vals is not read.
+    const float *dot_rows;
+    const float *dot_cols;
     int64_t M;
     int64_t K;
     int64_t N;

@@ -59,18 +59,25 @@ namespace {
 // chunks of colind/vals are loaded coalesced, one entry per lane (the next
 // chunk prefetched into registers while the current one is consumed), and
 // group g consumes entries g*G .. g*G+G-1 of each chunk, reading them from
-// the lanes that hold them.
+// the lanes that hold them.  FusedMM: the values are formed from row `row`
+// of X (held by each lane for its columns) and the entries' rows of Y.
 template <class S>
 __device__ inline void wave_range(const WorkerArgs &a, int lane, int g,
-                                  int64_t p0, int64_t p1, const BSrc &src,
+                                  int64_t row, int64_t p0, int64_t p1,
+                                  const BSrc &src, const BSrc &ysrc,
                                   const LaneCols<S> &lc, uint32_t row_bytes,
                                   float (&acc)[S::NV][S::VEC])
 {
     zero_acc<S>(acc);
+    float x[S::NV][S::VEC];
+    if constexpr (S::FUSED)
+        load_x_row<S>((const char *)a.dot_rows, row, row_bytes, lc, x);
     // positions past the range read the range's last entry (valid address)
     int64_t p = p0 + lane < p1 ? p0 + lane : p1 - 1;
     int32_t nc = a.colind[p];
-    float nvv = load_val<S::DT>(a.vals, p);
+    float nvv = 0.0f;
+    if constexpr (!S::FUSED)
+        nvv = load_val<S::DT>(a.vals, p);
     for (int64_t base = p0; base < p1; base += kWave) {
         const int n = p1 - base < kWave ? (int)(p1 - base) : kWave;
         const int32_t col = nc;
@@ -79,11 +86,15 @@ __device__ inline void wave_range(const WorkerArgs &a, int lane, int g,
         if (nb < p1) {
             p = nb + lane < p1 ? nb + lane : p1 - 1;
             nc = a.colind[p];
-            nvv = load_val<S::DT>(a.vals, p);
+            if constexpr (!S::FUSED)
+                nvv = load_val<S::DT>(a.vals, p);
         }
         int cnt = n - g * S::G;
         cnt = cnt < 0 ? 0 : (cnt > S::G ? S::G : cnt);
-        consume_lanes<S>(col, val, g * S::G, cnt, src, row_bytes, lc, acc);
+        if constexpr (S::FUSED)
+            consume_lanes_fused<S>(col, g * S::G, cnt, src, ysrc, row_bytes, lc, x, acc);
+        else
+            consume_lanes<S>(col, val, g * S::G, cnt, src, row_bytes, lc, acc);
     }
 }
 
@@ -142,15 +153,50 @@ __device__ inline bool medium_ready(const WorkerArgs &a, int64_t i, int64_t *row
 template <class S, bool ATOMIC>
 __device__ void do_range(const WorkerArgs &a, int lane, int g, int j,
                          int64_t row, int64_t p0, int64_t p1,
-                         const BSrc &src, uint32_t row_bytes)
+                         const BSrc &src, const BSrc &ysrc, uint32_t row_bytes)
 {
     for (int64_t col0 = 0; col0 < a.N; col0 += S::COLS) {
         const LaneCols<S> lc = lane_cols<S>(a.N, col0, j);
         float acc[S::NV][S::VEC];
-        wave_range<S>(a, lane, g, p0, p1, src, lc, row_bytes, acc);
+        wave_range<S>(a, lane, g, row, p0, p1, src, ysrc, lc, row_bytes, acc);
         reduce_groups<S>(acc);
         if (g == 0)
             emit_row<S, ATOMIC>(a.C, row, a.N, col0, j, acc);
+    }
+}
+
+// FusedMM form of issue() for a short tile: for each of the U staged
+// entries (slots past n repeat entry q) the gathers of Y_j and D_j and the
+// load of this lane's slice of X_i (rows are consecutive, so these mostly hit
+// the cache) are issued first; then each entry's value <X_i, Y_j> is formed
+// and the D_j vectors go into bt as the rows to accumulate.
+template <class S>
+__device__ inline void issue_fused(Batch<S> &bt, const WaveStage &ws,
+                                   const WorkerArgs &a, int64_t r0, int q,
+                                   int n, const BSrc &dsrc, const BSrc &ysrc,
+                                   uint32_t row_bytes, const LaneCols<S> &lc)
+{
+    typedef BLoad<S::DT, S::VEC> L;
+    typename L::raw yb[S::U][S::NV], xb[S::U][S::NV];
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+        const int e = u < n ? q + u : q;
+        const int32_t c = ws.ent[e].col;
+        const char *xrow = (const char *)a.dot_rows + (uint64_t)(r0 + ws.rid[e]) * row_bytes;
+#pragma unroll
+        for (int k = 0; k < S::NV; ++k) {
+            yb[u][k] = load_row_vec<S>(ysrc, c, row_bytes, lc, k);
+            xb[u][k] = L::load(xrow + lc.ofs[k]);
+            bt.buf[u][k] = load_row_vec<S>(dsrc, c, row_bytes, lc, k);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+        float x[S::NV][S::VEC];
+#pragma unroll
+        for (int k = 0; k < S::NV; ++k)
+            L::widen(xb[u][k], x[k]);
+        bt.v[u] = group_dot<S>(x, yb[u], lc);
     }
 }
 
@@ -159,7 +205,8 @@ __device__ void do_range(const WorkerArgs &a, int lane, int g, int j,
 template <class S>
 __device__ void do_short_tile(const WorkerArgs &a, WaveStage &ws, int lane,
                               int g, int j, int64_t r0, int P,
-                              const BSrc &src, uint32_t row_bytes)
+                              const BSrc &src, const BSrc &ysrc,
+                              uint32_t row_bytes)
 {
     const int T = P * S::R;
     const int64_t r = r0 + lane;
@@ -197,7 +244,7 @@ __device__ void do_short_tile(const WorkerArgs &a, WaveStage &ws, int lane,
             }
             const int64_t p = (int64_t)__shfl(s, l) + (e - __shfl(off, l));
             scol[i] = a.colind[p];
-            sval[i] = load_val<S::DT>(a.vals, p);
+            sval[i] = S::FUSED ? 0.0f : load_val<S::DT>(a.vals, p);
             srow[i] = l;
         }
     }
@@ -237,7 +284,10 @@ __device__ void do_short_tile(const WorkerArgs &a, WaveStage &ws, int lane,
         for (int q = beg; q < end; q += S::U) {
             const int n = end - q < S::U ? end - q : S::U;
             Batch<S> bt;
-            issue<S>(bt, ws.ent, q, n, src, row_bytes, lc);
+            if constexpr (S::FUSED)
+                issue_fused<S>(bt, ws, a, r0, q, n, src, ysrc, row_bytes, lc);
+            else
+                issue<S>(bt, ws.ent, q, n, src, row_bytes, lc);
 #pragma unroll
             for (int u = 0; u < S::U; ++u) {
                 accumulate<S>(bt, u, u < n, acc);
@@ -323,7 +373,7 @@ __device__ inline void do_item(const WorkerArgs &a, const ProductShape &ps,
                                WaveStage &ws, int lane, int g, int j,
                                int64_t d, int64_t n_ch, int64_t n_med,
                                int64_t n_long, const BSrc &src,
-                               uint32_t row_bytes)
+                               const BSrc &ysrc, uint32_t row_bytes)
 {
     int64_t row = 0, p0 = 0, p1 = 0;
     if (d < n_ch) {
@@ -331,20 +381,20 @@ __device__ inline void do_item(const WorkerArgs &a, const ProductShape &ps,
         // chunk was published; the atomic adds address it through the
         // published row, so they come after the clearing.
         if (wait_for([&]() { return chunk_ready(a, d, n_long, &row, &p0, &p1); }))
-            do_range<S, true>(a, lane, g, j, row, p0, p1, src, row_bytes);
+            do_range<S, true>(a, lane, g, j, row, p0, p1, src, ysrc, row_bytes);
         else
             note_fault(a, lane);
     } else if (d < n_ch + n_med) {
         if (wait_for([&]() { return medium_ready(a, d - n_ch, &row); }))
             do_range<S, false>(a, lane, g, j, row, a.rowptr[row],
-                               a.rowptr[row + 1], src, row_bytes);
+                               a.rowptr[row + 1], src, ysrc, row_bytes);
         else
             note_fault(a, lane);
     } else {
         const int64_t t = d - n_ch - n_med;
         do_short_tile<S>(a, ws, lane, g, j,
                          ps.rows_static + t * (int64_t)(ps.dyn_passes * S::R),
-                         ps.dyn_passes, src, row_bytes);
+                         ps.dyn_passes, src, ysrc, row_bytes);
     }
 }
 
@@ -405,6 +455,15 @@ void call_kernel(WorkerArgs a, ProductShape ps)
         src.rsrc = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<void *>(a.B), (short)0,
             (int)(uint32_t)(a.K * a.N * S::ESZ), kBufferWord3);
+    // FusedMM: Y (K x N, like B) is gathered the same way.
+    BSrc ysrc = src;
+    if constexpr (S::FUSED) {
+        ysrc.base = (const char *)a.dot_cols;
+        if constexpr (S::BUF)
+            ysrc.rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float *>(a.dot_cols), (short)0,
+                (int)(uint32_t)(a.K * a.N * S::ESZ), kBufferWord3);
+    }
 
     if (!planner) {
         // plan_grid is a multiple of 8, so product block b runs on XCD b % 8
@@ -413,7 +472,7 @@ void call_kernel(WorkerArgs a, ProductShape ps)
                               kWavesPerBlock + wid;
         if (w < ps.first)
             do_short_tile<S>(a, ws, lane, g, j, w * (int64_t)(ps.passes * S::R),
-                             ps.passes, src, row_bytes);
+                             ps.passes, src, ysrc, row_bytes);
     }
 
     int64_t n_med = 0, n_long = 0, n_ch = 0;
@@ -439,7 +498,7 @@ void call_kernel(WorkerArgs a, ProductShape ps)
             break;
         if (lane == 0)
             next = atomicAdd(ctr, 1u);
-        do_item<S>(a, ps, ws, lane, g, j, d, n_ch, n_med, n_long, src, row_bytes);
+        do_item<S>(a, ps, ws, lane, g, j, d, n_ch, n_med, n_long, src, ysrc, row_bytes);
     }
 }
 
@@ -498,21 +557,21 @@ hipError_t launch_shape(const WorkerArgs &a, hipStream_t stream,
     return hipGetLastError();
 }
 
-template <int DT, int VEC, bool BUF>
+template <int DT, int VEC, bool BUF, bool FUSED = false>
 hipError_t launch_vec(int group, int nv, const WorkerArgs &a, hipStream_t s,
                       hipEvent_t e0, hipEvent_t e1)
 {
     switch (group) {
-    case 1: return launch_shape<Shape<DT, VEC, 1, 1, BUF>>(a, s, e0, e1);
-    case 2: return launch_shape<Shape<DT, VEC, 2, 1, BUF>>(a, s, e0, e1);
-    case 4: return launch_shape<Shape<DT, VEC, 4, 1, BUF>>(a, s, e0, e1);
-    case 8: return launch_shape<Shape<DT, VEC, 8, 1, BUF>>(a, s, e0, e1);
-    case 16: return launch_shape<Shape<DT, VEC, 16, 1, BUF>>(a, s, e0, e1);
-    case 32: return launch_shape<Shape<DT, VEC, 32, 1, BUF>>(a, s, e0, e1);
+    case 1: return launch_shape<Shape<DT, VEC, 1, 1, BUF, FUSED>>(a, s, e0, e1);
+    case 2: return launch_shape<Shape<DT, VEC, 2, 1, BUF, FUSED>>(a, s, e0, e1);
+    case 4: return launch_shape<Shape<DT, VEC, 4, 1, BUF, FUSED>>(a, s, e0, e1);
+    case 8: return launch_shape<Shape<DT, VEC, 8, 1, BUF, FUSED>>(a, s, e0, e1);
+    case 16: return launch_shape<Shape<DT, VEC, 16, 1, BUF, FUSED>>(a, s, e0, e1);
+    case 32: return launch_shape<Shape<DT, VEC, 32, 1, BUF, FUSED>>(a, s, e0, e1);
     case 64:
-        if (nv == 1) return launch_shape<Shape<DT, VEC, 64, 1, BUF>>(a, s, e0, e1);
-        if (nv == 2) return launch_shape<Shape<DT, VEC, 64, 2, BUF>>(a, s, e0, e1);
-        return launch_shape<Shape<DT, VEC, 64, 4, BUF>>(a, s, e0, e1);
+        if (nv == 1) return launch_shape<Shape<DT, VEC, 64, 1, BUF, FUSED>>(a, s, e0, e1);
+        if (nv == 2) return launch_shape<Shape<DT, VEC, 64, 2, BUF, FUSED>>(a, s, e0, e1);
+        return launch_shape<Shape<DT, VEC, 64, 4, BUF, FUSED>>(a, s, e0, e1);
     default: return hipErrorInvalidValue;
     }
 }
@@ -571,6 +630,12 @@ hipError_t launch_dtype(const WorkerConfig &cfg, const WorkerArgs &a,
     return hipErrorInvalidValue;
 }
 
+bool fused_fits(const WorkerConfig &cfg, int64_t N)
+{
+    return cfg.dtype == SPMM_DTYPE_F32 && cfg.vec == 4 &&
+           N <= (int64_t)cfg.group * cfg.vec * cfg.nv;
+}
+
 hipError_t launch_call(const WorkerConfig &cfg, const WorkerArgs &a,
                        hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
@@ -578,7 +643,15 @@ hipError_t launch_call(const WorkerConfig &cfg, const WorkerArgs &a,
     // is below 4 GiB, otherwise through flat 64-bit addresses.
     const int esz = cfg.dtype == SPMM_DTYPE_BF16 ? 2 : 4;
     const uint64_t b_bytes = (uint64_t)a.K * (uint64_t)a.N * (uint64_t)esz;
-    if (b_bytes < 0xFFFFFFFFull)
+    const bool buf = b_bytes < 0xFFFFFFFFull;
+    if (a.dot_rows != nullptr) {
+        // FusedMM: fp32, 16-byte vectors, the whole row in one column pass.
+        if (!fused_fits(cfg, a.N) || a.dot_cols == nullptr)
+            return hipErrorInvalidValue;
+        return buf ? launch_vec<SPMM_DTYPE_F32, 4, true, true>(cfg.group, cfg.nv, a, s, e0, e1)
+                   : launch_vec<SPMM_DTYPE_F32, 4, false, true>(cfg.group, cfg.nv, a, s, e0, e1);
+    }
+    if (buf)
         return launch_dtype<true>(cfg, a, s, e0, e1);
     return launch_dtype<false>(cfg, a, s, e0, e1);
 }

@@ -4,6 +4,10 @@ Page: [IntelMax] "Performance Optimization of Deep Learning Sparse Matrix
 Kernels on Intel Max Series GPU", the FusedMM operation (Fig. 6,
 Algorithm 3).
 
+Two routes: one launch that forms each value where it is used (fp32, N a
+multiple of 4 up to 1024, operands 16-byte aligned), and otherwise SDDMM
+into a value array followed by the product.  Both are checked here.
+
 Bar: |E_gpu - E_ref| <= 2 tol(N) T + 1e-6 per element, with the bound
 T[i,n] = sum_p S_p |D_jn| and tol(N) = max(1e-5, N 2^-23): each SDDMM value
 is off by at most ~N 2^-24 S_p before it weights D_j (its rounding to fp32
@@ -31,20 +35,31 @@ def tol(N):
     return 2 * max(1e-5, N * 2.0 ** -23)
 
 
-def run_fused(rowptr, colind, C, B, D, M, K, N, fill=float("nan")):
+def _dev(x, shift=0):
+    """x on the GPU; shift > 0 places it `shift` floats past a 16-byte
+    boundary (a view into a larger buffer)."""
+    flat = torch.from_numpy(np.ascontiguousarray(x).reshape(-1))
+    if not shift:
+        return flat.cuda()
+    buf = torch.zeros(flat.numel() + shift, dtype=torch.float32, device="cuda")
+    buf[shift:] = flat.cuda()
+    return buf[shift:]
+
+
+def run_fused(rowptr, colind, C, B, D, M, K, N, fill=float("nan"), shift=0):
     rp = torch.from_numpy(np.ascontiguousarray(rowptr, np.int32)).cuda()
     ci = torch.from_numpy(np.ascontiguousarray(colind, np.int32)).cuda()
     E = torch.full((M * N,), fill, dtype=torch.float32, device="cuda")
     nnz = int(rowptr[-1]) - int(rowptr[0])
-    sdl.fusedmm_csr_f32(rp, ci, torch.from_numpy(C).cuda(), torch.from_numpy(B).cuda(),
-                        torch.from_numpy(D).cuda(), E, M, K, N, nnz)
+    sdl.fusedmm_csr_f32(rp, ci, _dev(C, shift), _dev(B, shift), torch.from_numpy(D).cuda(),
+                        E, M, K, N, nnz)
     torch.cuda.synchronize()
     assert sdl.stream_faults() == 0
     return E.cpu().numpy().reshape(M, N)
 
 
-def check(rowptr, colind, C, B, D, M, K, N, what=""):
-    E = run_fused(rowptr, colind, C, B, D, M, K, N)
+def check(rowptr, colind, C, B, D, M, K, N, what="", shift=0):
+    E = run_fused(rowptr, colind, C, B, D, M, K, N, shift=shift)
     Eref, T = oracle.fusedmm_ref(rowptr, colind, C, B, D, N)
     bad = ~(np.abs(E.astype(np.float64) - Eref) <= tol(N) * T + 1e-6)
     if bad.any():
@@ -78,7 +93,7 @@ def test_worked_example_bitwise():
 EDGE = [0, 1, 2, 3, 9, 16, 17, 64, 200, 257, 1100, 3000]
 
 
-@pytest.mark.parametrize("N", [1, 4, 8, 32, 64, 128, 256, 512])
+@pytest.mark.parametrize("N", [1, 3, 4, 6, 8, 32, 64, 128, 256, 512, 1024, 1100])
 def test_edge_rows(N):
     """Rows of every kind the product routes (empty, short, medium, long
     rows cut into chunks)."""
@@ -88,6 +103,19 @@ def test_edge_rows(N):
     lengths[:len(EDGE)] = EDGE
     rp, ci = pattern(lengths, K, seed=N)
     check(rp, ci, dense(rng, M, N), dense(rng, K, N), dense(rng, K, N), M, K, N, f"N={N}")
+
+
+@pytest.mark.parametrize("N", [8, 64, 256])
+def test_unaligned_operands(N):
+    """C and B one float past a 16-byte boundary take the two-launch route
+    (whose SDDMM then reads single elements, another summation order); both
+    routes are held to the same bound."""
+    rng = np.random.default_rng(N + 7)
+    M, K = 300, 900
+    rp, ci = pattern(rng.integers(0, 50, M), K, seed=N + 7)
+    C, B, D = dense(rng, M, N), dense(rng, K, N), dense(rng, K, N)
+    check(rp, ci, C, B, D, M, K, N, f"N={N} unaligned", shift=1)
+    check(rp, ci, C, B, D, M, K, N, f"N={N} aligned")
 
 
 def test_view_and_empty():
@@ -113,8 +141,10 @@ def test_no_entries():
 
 
 def test_equals_sddmm_then_spmm():
-    """The fused call equals, bit for bit, SDDMM into an array followed by
-    the product with those values (the same kernels in the same order)."""
+    """The one-launch call equals, bit for bit, SDDMM into an array followed
+    by the product with those values, on rows that are not split: at N = 64
+    both use 16-lane groups, so the fused worker forms each value in the
+    SDDMM kernel's order and accumulates it as the product does."""
     rng = np.random.default_rng(5)
     M, K, N = 1500, 1200, 64
     rp, ci = pattern(rng.integers(0, 40, M), K, seed=5)
