@@ -20,11 +20,14 @@
 //     batch that runs past 64 rows (empty rows) moves the window on;
 //   * the 64 dot products are computed by R = 64/G groups of G lanes: for
 //     entry k the group reads C_i and B_j as 16-byte vectors (one per lane,
-//     VEC elements), multiplies them element-wise, sums the lane's part,
-//     and the group adds its G parts with butterfly shuffles; U entries per
-//     group are in flight at once;
-//   * the 64 results are gathered in LDS and written with one coalesced
-//     store.
+//     VEC elements), multiplies them element-wise and sums the lane's part;
+//     U entries per group are in flight at once, and when all of them lie in
+//     one row (long rows) the C_i vector is loaded once for the U;
+//   * the group adds its G parts with butterfly shuffles, and the 64 results
+//     are gathered in LDS and written with one coalesced store; or, for one
+//     64-lane group of fp32 rows, each lane keeps its parts of all 64 entries
+//     and a reduce-scatter leaves entry u's total in one lane (63 shuffles
+//     per lane instead of 6 per entry), summed in the butterfly's order.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -77,11 +80,70 @@ struct SdShape {
     static constexpr int R = kWave / G_;   // groups per wavefront
     static constexpr int COLS = G_ * VEC_; // columns per pass over a row
     static constexpr int U = 4;            // entries per group in flight
-    static_assert((kWave / R) % U == 0, "a batch is a whole number of steps");
+    static constexpr int LOGG = G_ == 1 ? 0 : G_ == 2 ? 1 : G_ == 4 ? 2 : G_ == 8 ? 3
+                              : G_ == 16 ? 4 : G_ == 32 ? 5 : 6;
+    static_assert((1 << LOGG) == G_, "G is a power of two up to 64");
+    static_assert(G_ % U == 0, "a group's G entries are a whole number of steps");
+    // RS: one 64-lane group per wavefront, whose 64 dot products are
+    // finished by a reduce-scatter (fp32 operands; with bf16 the 64 partial
+    // sums per lane do not fit beside the wider loads).  It holds 64 partial
+    // sums per lane: ask for registers that still allow 3 wavefronts per SIMD.
+    static constexpr bool RS = G_ == kWave && DT_ == SPMM_DTYPE_F32;
+    static constexpr int MIN_WAVES = RS ? 3 : 1;
 };
 
+// This lane's parts of NU dot products <C row ci[u], B row bj[u]> (offsets
+// in elements): over the column passes, a chain of fused multiply-adds per
+// vector; lanes past the end of the row read its last vector and contribute
+// nothing.  ONE_ROW: all ci[u] are equal, and the C vector is loaded once.
+template <class S, bool ONE_ROW, int NU>
+__device__ inline void dots(const void *__restrict__ C, const void *__restrict__ B,
+                            const int64_t *ci, const int64_t *bj, int64_t N,
+                            int jl, float *part)
+{
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+        part[u] = 0.0f;
+    for (int64_t col0 = 0; col0 < N; col0 += S::COLS) {
+        const int64_t c = col0 + (int64_t)jl * S::VEC;
+        const bool in = c < N;
+        const int64_t cc = in ? c : N - S::VEC;
+        constexpr int NC = ONE_ROW ? 1 : NU;
+        float cv[NC][S::VEC], bv[NU][S::VEC];
+#pragma unroll
+        for (int u = 0; u < NC; ++u)
+            RowLoad<S::DT, S::VEC>::load(C, ci[u] + cc, cv[u]);
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+            RowLoad<S::DT, S::VEC>::load(B, bj[u] + cc, bv[u]);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            float d = 0.0f;
+#pragma unroll
+            for (int x = 0; x < S::VEC; ++x)
+                d = __builtin_fmaf(cv[ONE_ROW ? 0 : u][x], bv[u][x], d);
+            part[u] += in ? d : 0.0f;
+        }
+    }
+}
+
+// Rows of C and B (element offsets) of group g's entries u0 .. u0+U-1 of
+// the batch (entry k = u * R + g, held by lane k).
 template <class S>
-__global__ __launch_bounds__(kBlock) void sddmm_kernel(
+__device__ inline void entry_rows(int64_t row, int32_t col, int64_t N, int u0,
+                                  int g, int64_t (&ci)[S::U], int64_t (&bj)[S::U])
+{
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+        const int k = (u0 + u) * S::R + g;
+        ci[u] = __shfl(row, k) * N;
+        bj[u] = (int64_t)__shfl(col, k) * N;
+    }
+}
+
+template <class S>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(S::MIN_WAVES)))
+void sddmm_kernel(
     const int32_t *__restrict__ rowptr, const int32_t *__restrict__ colind,
     const void *__restrict__ C, const void *__restrict__ B,
     float *__restrict__ A, int64_t M, int64_t N, int64_t nnz, int64_t span)
@@ -105,64 +167,80 @@ __global__ __launch_bounds__(kBlock) void sddmm_kernel(
     int64_t i_cur = find_row(rowptr, M, base + s0, lane);
 
     for (int64_t e0 = s0; e0 < s1; e0 += kWave) {
-        const int64_t e = e0 + lane;
-        const bool live = e < s1;
-        const int64_t pe = base + (live ? e : s1 - 1);
+        const int64_t pe = base + (e0 + lane < s1 ? e0 + lane : s1 - 1);
         const int32_t col = colind[pe];
 
         const int64_t row = row_in_window(rowptr, M, i_cur, pe, lane);
         i_cur = __shfl(row, kWave - 1);
 
-        // The 64 dot products: group g takes entries k = u * R + g.
-        for (int u0 = 0; u0 < kWave / S::R; u0 += S::U) {
-            float part[S::U];
+        if constexpr (S::RS) {
+            // One group (the whole wavefront) takes all 64 entries; part[u]
+            // is this lane's part of entry u's dot product.
+            float part[S::G];
 #pragma unroll
-            for (int u = 0; u < S::U; ++u)
-                part[u] = 0.0f;
-            int64_t ci[S::U], bj[S::U];
-#pragma unroll
-            for (int u = 0; u < S::U; ++u) {
-                const int k = (u0 + u) * S::R + g;
-                ci[u] = __shfl(row, k) * N;
-                bj[u] = (int64_t)__shfl(col, k) * N;
+            for (int u0 = 0; u0 < S::G; u0 += S::U) {
+                int64_t ci[S::U], bj[S::U];
+                entry_rows<S>(row, col, N, u0, g, ci, bj);
+                if (__all(ci[0] == ci[S::U - 1]))
+                    dots<S, true, S::U>(C, B, ci, bj, N, jl, part + u0);
+                else
+                    dots<S, false, S::U>(C, B, ci, bj, N, jl, part + u0);
+                // one step's loads at a time (the steps are unrolled only so
+                // that part[] has fixed indices)
+                __builtin_amdgcn_sched_barrier(0);
             }
-            for (int64_t col0 = 0; col0 < N; col0 += S::COLS) {
-                // lanes past the end of the row read its last vector and
-                // contribute nothing
-                const int64_t c = col0 + (int64_t)jl * S::VEC;
-                const bool in = c < N;
-                const int64_t cc = in ? c : N - S::VEC;
-                float cv[S::U][S::VEC], bv[S::U][S::VEC];
+            // Reduce-scatter over the 64 lanes: at each stage a lane keeps
+            // half of its partial sums and sends the other half to the lane
+            // that differs in one bit, adding what it receives.  The lowest
+            // bit goes first, so each total is added up in the same order as
+            // the butterfly below; the total of entry u ends in lane
+            // bitrev(u).  63 shuffles per lane instead of 6 per entry.
+#pragma unroll
+            for (int b = 0; b < S::LOGG; ++b) {
+                const int h = 1 << b;                 // partner distance
+                const int half = S::G >> (b + 1);     // values kept after this stage
+                const bool upper = (jl & h) != 0;
+#pragma unroll
+                for (int i = 0; i < half; ++i) {
+                    const float send = upper ? part[i] : part[i + half];
+                    const float keep = upper ? part[i + half] : part[i];
+                    part[i] = keep + __shfl_xor(send, h);
+                }
+            }
+            const int u = (int)(__builtin_bitreverse32((uint32_t)jl) >> (32 - S::LOGG));
+            const int64_t eu = e0 + (int64_t)u * S::R + g;
+            if (eu < s1)
+                A[eu] = part[0];
+        } else {
+            // Group g takes entries k = u * R + g; each step's U dot products
+            // are finished by a butterfly over the group's lanes (lane l adds
+            // lane l ^ 1, then l ^ 2, ...), and the 64 results are gathered in
+            // LDS for one coalesced store.
+            for (int u0 = 0; u0 < S::G; u0 += S::U) {
+                int64_t ci[S::U], bj[S::U];
+                entry_rows<S>(row, col, N, u0, g, ci, bj);
+                float part[S::U];
+                if (__all(ci[0] == ci[S::U - 1]))
+                    dots<S, true, S::U>(C, B, ci, bj, N, jl, part);
+                else
+                    dots<S, false, S::U>(C, B, ci, bj, N, jl, part);
+                // this batch's results go to res only after every lane has
+                // read the previous batch's
+                __builtin_amdgcn_wave_barrier();
 #pragma unroll
                 for (int u = 0; u < S::U; ++u) {
-                    RowLoad<S::DT, S::VEC>::load(C, ci[u] + cc, cv[u]);
-                    RowLoad<S::DT, S::VEC>::load(B, bj[u] + cc, bv[u]);
-                }
+                    float d = part[u];
 #pragma unroll
-                for (int u = 0; u < S::U; ++u) {
-                    float d = 0.0f;
-#pragma unroll
-                    for (int x = 0; x < S::VEC; ++x)
-                        d = __builtin_fmaf(cv[u][x], bv[u][x], d);
-                    part[u] += in ? d : 0.0f;
+                    for (int off = 1; off < S::G; off <<= 1)
+                        d += __shfl_xor(d, off);
+                    if (jl == 0)
+                        res[wid][(u0 + u) * S::R + g] = d;
                 }
             }
-            // this batch's results go to res only after every lane has
-            // read the previous batch's
-            __builtin_amdgcn_wave_barrier();
-#pragma unroll
-            for (int u = 0; u < S::U; ++u) {
-                float d = part[u];
-#pragma unroll
-                for (int off = 1; off < S::G; off <<= 1)
-                    d += __shfl_xor(d, off);
-                if (jl == 0)
-                    res[wid][(u0 + u) * S::R + g] = d;
-            }
+            __builtin_amdgcn_wave_barrier();  // all 64 results are in res
+            if (e0 + lane < s1)
+                A[e0 + lane] = res[wid][lane];
         }
-        __builtin_amdgcn_wave_barrier();  // all 64 results are in res
-        if (live)
-            A[e] = res[wid][lane];
     }
 }
 
