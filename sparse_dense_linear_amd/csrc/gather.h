@@ -377,7 +377,10 @@ __device__ inline void zero_acc(float (&acc)[S::NV][S::VEC])
             acc[k][x] = 0.0f;
 }
 
-// Store (or atomically add) this lane's columns of one C row.
+// Store (or atomically add) this lane's columns of one C row.  Plain stores
+// are nontemporal: C is written once and not read again by the call, so its
+// lines need not displace gathered B rows from the caches (measured faster
+// on every workload).
 template <class S, bool ATOMIC>
 __device__ inline void emit_row(float *C, int64_t row, int64_t N, int64_t col0,
                                 int j, const float (&acc)[S::NV][S::VEC])
@@ -396,13 +399,13 @@ __device__ inline void emit_row(float *C, int64_t row, int64_t N, int64_t col0,
 #pragma unroll
             for (int x = 0; x < S::VEC; x += 4) {
                 f32x4 w = {acc[k][x], acc[k][x + 1], acc[k][x + 2], acc[k][x + 3]};
-                *(f32x4 *)(crow + c + x) = w;
+                __builtin_nontemporal_store(w, (f32x4 *)(crow + c + x));
             }
         } else if constexpr (S::VEC == 2) {
             f32x2 w = {acc[k][0], acc[k][1]};
-            *(f32x2 *)(crow + c) = w;
+            __builtin_nontemporal_store(w, (f32x2 *)(crow + c));
         } else {
-            crow[c] = acc[k][0];
+            __builtin_nontemporal_store(acc[k][0], crow + c);
         }
     }
 }

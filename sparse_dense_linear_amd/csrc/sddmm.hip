@@ -210,7 +210,7 @@ void sddmm_kernel(
             const int u = (int)(__builtin_bitreverse32((uint32_t)jl) >> (32 - S::LOGG));
             const int64_t eu = e0 + (int64_t)u * S::R + g;
             if (eu < s1)
-                A[eu] = part[0];
+                __builtin_nontemporal_store(part[0], A + eu);  // written once
         } else {
             // Group g takes entries k = u * R + g; each step's U dot products
             // are finished by a butterfly over the group's lanes (lane l adds
@@ -239,7 +239,7 @@ void sddmm_kernel(
             }
             __builtin_amdgcn_wave_barrier();  // all 64 results are in res
             if (e0 + lane < s1)
-                A[e0 + lane] = res[wid][lane];
+                __builtin_nontemporal_store(res[wid][lane], A + e0 + lane);
         }
     }
 }
