@@ -365,9 +365,13 @@ struct ProductShape {
     int64_t static_waves;  // product wavefronts
 };
 
-// One queued item: [0, n_ch) long-row chunks, then medium rows, then the
-// short tiles after the static ones (heaviest kinds first, the smallest
-// items last so that the queues drain evenly).
+// One queued item: [0, n_ch) long-row chunks (the heaviest items first),
+// then, for the product, the short tiles after the static ones and last the
+// medium rows; for FusedMM medium rows before short tiles.  Ending on medium
+// rows (one wavefront per row, every gather slot busy) drains the queues
+// faster than ending on short tiles (a few rows per lane group, batches
+// part empty): measured 6 % faster on the power-law workload; FusedMM,
+// with two gathers per entry, measured the other way.
 template <class S>
 __device__ inline void do_item(const WorkerArgs &a, const ProductShape &ps,
                                WaveStage &ws, int lane, int g, int j,
@@ -384,17 +388,23 @@ __device__ inline void do_item(const WorkerArgs &a, const ProductShape &ps,
             do_range<S, true>(a, lane, g, j, row, p0, p1, src, ysrc, row_bytes);
         else
             note_fault(a, lane);
-    } else if (d < n_ch + n_med) {
-        if (wait_for([&]() { return medium_ready(a, d - n_ch, &row); }))
-            do_range<S, false>(a, lane, g, j, row, a.rowptr[row],
-                               a.rowptr[row + 1], src, ysrc, row_bytes);
-        else
-            note_fault(a, lane);
     } else {
-        const int64_t t = d - n_ch - n_med;
-        do_short_tile<S>(a, ws, lane, g, j,
-                         ps.rows_static + t * (int64_t)(ps.dyn_passes * S::R),
-                         ps.dyn_passes, src, ysrc, row_bytes);
+        // medium rows, then short tiles (FusedMM); short tiles, then medium
+        // rows (product)
+        const int64_t e = d - n_ch;
+        const int64_t m = S::FUSED ? e : e - ps.n_dyn_tiles;
+        if (m >= 0 && m < n_med) {
+            if (wait_for([&]() { return medium_ready(a, m, &row); }))
+                do_range<S, false>(a, lane, g, j, row, a.rowptr[row],
+                                   a.rowptr[row + 1], src, ysrc, row_bytes);
+            else
+                note_fault(a, lane);
+        } else {
+            const int64_t t = S::FUSED ? e - n_med : e;
+            do_short_tile<S>(a, ws, lane, g, j,
+                             ps.rows_static + t * (int64_t)(ps.dyn_passes * S::R),
+                             ps.dyn_passes, src, ysrc, row_bytes);
+        }
     }
 }
 
@@ -405,7 +415,7 @@ __device__ inline void do_item(const WorkerArgs &a, const ProductShape &ps,
 // logical product wavefront w takes tile w, for w < first), which needs no
 // plan.  Then every wavefront, the planners included, takes the remaining
 // items from kQueues work queues: queue q hands out items q, q + kQueues,
-// ... of the list [long-row chunks | medium rows | short tiles], so every
+// ... of the list [long-row chunks | short tiles | medium rows], so every
 // queue holds the same mix, and a wavefront that started late or drew slow
 // items simply takes fewer.
 template <class S>
