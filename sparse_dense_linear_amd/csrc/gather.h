@@ -141,8 +141,12 @@ template <> __device__ inline float load_val<SPMM_DTYPE_BF16>(const void *vals, 
 
 // Compile-time shape of one worker variant.  FUSED: the FusedMM variant,
 // whose entry values are computed on the fly (two gathers per entry, so
-// half as many entries in flight).
-template <int DT_, int VEC_, int G_, int NV_, bool BUF_, bool FUSED_ = false>
+// half as many entries in flight).  DEEP: the planned product may keep 16
+// gathers in flight per lane when one 64-lane group takes a whole fp32 row
+// of B, at 3 wavefronts per SIMD instead of 4 (measured 6 % faster on the
+// pruned workload; 32-lane groups, bf16 rows and FusedMM measured slower).
+template <int DT_, int VEC_, int G_, int NV_, bool BUF_, bool FUSED_ = false,
+          bool DEEP_ = false>
 struct Shape {
     static constexpr bool BUF = BUF_;   // B addressed through a buffer resource
     static constexpr bool FUSED = FUSED_;
@@ -152,8 +156,11 @@ struct Shape {
     static constexpr int NV = NV_;
     static constexpr int R = kWave / G_;          // groups per wavefront
     static constexpr int COLS = G_ * VEC_ * NV_;  // columns per column pass
-    static constexpr int U0 = NV_ == 1 ? 8 : (NV_ == 2 ? 4 : 2);
+    static constexpr bool WIDE = DEEP_ && !FUSED_ && G_ == kWave && NV_ == 1 &&
+                                 DT_ == SPMM_DTYPE_F32;
+    static constexpr int U0 = WIDE ? 16 : (NV_ == 1 ? 8 : (NV_ == 2 ? 4 : 2));
     static constexpr int U = FUSED_ ? (U0 / 2 > 1 ? U0 / 2 : 1) : U0;  // entries in flight
+    static constexpr int MIN_WAVES = WIDE ? 3 : 4;   // wavefronts per SIMD
     static constexpr int ESZ = ElemSize<DT_>::v;
 };
 

@@ -419,7 +419,7 @@ __device__ inline void do_item(const WorkerArgs &a, const ProductShape &ps,
 // queue holds the same mix, and a wavefront that started late or drew slow
 // items simply takes fewer.
 template <class S>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(S::MIN_WAVES)))
 void call_kernel(WorkerArgs a, ProductShape ps)
 {
     if (a.vals_relative)  // entry p's value sits at vals[p - rowptr[0]]
@@ -582,7 +582,7 @@ hipError_t launch_vec(int group, int nv, const WorkerArgs &a, hipStream_t s,
     case 16: return launch_shape<Shape<DT, VEC, 16, 1, BUF, FUSED>>(a, s, e0, e1);
     case 32: return launch_shape<Shape<DT, VEC, 32, 1, BUF, FUSED>>(a, s, e0, e1);
     case 64:
-        if (nv == 1) return launch_shape<Shape<DT, VEC, 64, 1, BUF, FUSED>>(a, s, e0, e1);
+        if (nv == 1) return launch_shape<Shape<DT, VEC, 64, 1, BUF, FUSED, true>>(a, s, e0, e1);
         if (nv == 2) return launch_shape<Shape<DT, VEC, 64, 2, BUF, FUSED>>(a, s, e0, e1);
         return launch_shape<Shape<DT, VEC, 64, 4, BUF, FUSED>>(a, s, e0, e1);
     default: return hipErrorInvalidValue;
