@@ -249,6 +249,20 @@ spmm_status_t fusedmm_csr_f32(const int32_t *rowptr, const int32_t *colind,
                               int64_t nnz, void *stream);
 
 /*
+ * FusedMM as fusedmm_csr_f32 with C, B and D given as bf16 bit patterns
+ * (uint16), widened exactly to fp32; each value <C_i, B_j> is formed and
+ * used in fp32, the sums are fp32, and E is fp32.  One launch; shapes it
+ * does not cover (N not a multiple of 8 or above 1024, or C, B, D, E not
+ * 16-byte aligned) return SPMM_ERROR_UNSUPPORTED with nothing launched.
+ * nnz == 0: E becomes zero.  Other errors and ownership as for the product.
+ */
+spmm_status_t fusedmm_csr_bf16in_f32acc(const int32_t *rowptr,
+                                        const int32_t *colind, const uint16_t *C,
+                                        const uint16_t *B, const uint16_t *D,
+                                        float *E, int64_t M, int64_t K,
+                                        int64_t N, int64_t nnz, void *stream);
+
+/*
  * Health check for tests.  Inside a call, product wavefronts poll for the
  * plan entries they need while the plan workgroups of the same launch write
  * them; each poll is bounded (about a second), and an item whose entry

@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     Tuning,
     fusedmm,
     fusedmm_csr_f32,
+    fusedmm_csr_bf16in_f32acc,
     lib,
     lib_path,
     plan_export,

@@ -80,9 +80,10 @@ def lib() -> ctypes.CDLL:
     L.sddmm_csr_f32.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
     L.sddmm_csr_bf16in_f32acc.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
     L.fusedmm_csr_f32.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
+    L.fusedmm_csr_bf16in_f32acc.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
     L.spmm_csr_eb.argtypes = [I32, P, P, P, P, P, I64, I64, I64, P]
     for name in ("sddmm_csr_f32", "sddmm_csr_bf16in_f32acc", "fusedmm_csr_f32",
-                 "spmm_csr_eb"):
+                 "fusedmm_csr_bf16in_f32acc", "spmm_csr_eb"):
         getattr(L, name).restype = I32
     for name in ("spmm_csr_f32", "spmm_csr_bf16in_f32acc", "spmm_csr_tuned",
                  "spmm_resolve_tuning", "spmm_plan_export", "spmm_timing_enable",
@@ -278,10 +279,7 @@ def sddmm(rowptr, colind, C, B, stream=None):
     return A
 
 
-def fusedmm_csr_f32(rowptr, colind, C, B, D, E, M: int, K: int, N: int,
-                    nnz: int, stream=None) -> None:
-    """E_i = sum_p <C_i, B_colind[p]> D_colind[p] over the CSR pattern, fp32
-    (fusedmm_csr_f32).  nnz must be rowptr[M] - rowptr[0]."""
+def _check_fusedmm(rowptr, colind, C, B, D, E, M, K, N, nnz, in_types):
     torch = _torch()
     dev = E.device
     for name, t in {"rowptr": rowptr, "colind": colind, "C": C, "B": B, "D": D,
@@ -294,27 +292,56 @@ def fusedmm_csr_f32(rowptr, colind, C, B, D, E, M: int, K: int, N: int,
             raise ValueError(f"{name} must be contiguous")
     if rowptr.dtype != torch.int32 or colind.dtype != torch.int32:
         raise TypeError("rowptr and colind must be int32")
-    for name, t in {"C": C, "B": B, "D": D, "E": E}.items():
-        if t.dtype != torch.float32:
-            raise TypeError(f"{name} must be float32")
+    for name, t in {"C": C, "B": B, "D": D}.items():
+        if t.dtype not in in_types:
+            raise TypeError(f"{name} must be one of {in_types}")
+    if E.dtype != torch.float32:
+        raise TypeError("E must be float32")
     if rowptr.numel() != M + 1:
         raise ValueError("rowptr must hold M+1 entries")
     if C.numel() != M * N or B.numel() != K * N or D.numel() != K * N or E.numel() != M * N:
         raise ValueError("C and E must hold M*N, B and D K*N elements")
     if nnz < 0 or nnz > colind.numel():
         raise ValueError("nnz must be in [0, len(colind)]")
+    return dev
+
+
+def fusedmm_csr_f32(rowptr, colind, C, B, D, E, M: int, K: int, N: int,
+                    nnz: int, stream=None) -> None:
+    """E_i = sum_p <C_i, B_colind[p]> D_colind[p] over the CSR pattern, fp32
+    (fusedmm_csr_f32).  nnz must be rowptr[M] - rowptr[0]."""
+    torch = _torch()
+    dev = _check_fusedmm(rowptr, colind, C, B, D, E, M, K, N, nnz, (torch.float32,))
     _check(lib().fusedmm_csr_f32(_ptr(rowptr), _ptr(colind), _ptr(C), _ptr(B),
                                  _ptr(D), _ptr(E), M, K, N, nnz,
                                  _stream_handle(dev, stream)), "fusedmm_csr_f32")
 
 
+def fusedmm_csr_bf16in_f32acc(rowptr, colind, C, B, D, E, M: int, K: int,
+                              N: int, nnz: int, stream=None) -> None:
+    """FusedMM with bf16 C, B and D (torch.bfloat16 or int16/uint16 bits),
+    fp32 values, accumulation and E (fusedmm_csr_bf16in_f32acc)."""
+    torch = _torch()
+    bf = (torch.bfloat16, torch.int16, torch.uint16)
+    dev = _check_fusedmm(rowptr, colind, C, B, D, E, M, K, N, nnz, bf)
+    _check(lib().fusedmm_csr_bf16in_f32acc(_ptr(rowptr), _ptr(colind), _ptr(C),
+                                           _ptr(B), _ptr(D), _ptr(E), M, K, N, nnz,
+                                           _stream_handle(dev, stream)),
+           "fusedmm_csr_bf16in_f32acc")
+
+
 def fusedmm(rowptr, colind, C, B, D, stream=None):
-    """Allocate E and compute FusedMM (rowptr[0] must be 0)."""
+    """Allocate E and compute FusedMM; the element type follows C
+    (rowptr[0] must be 0)."""
     torch = _torch()
     M, N = C.shape
     K = B.shape[0]
     E = torch.empty((M, N), dtype=torch.float32, device=C.device)
-    fusedmm_csr_f32(rowptr, colind, C, B, D, E, M, K, N, colind.numel(), stream)
+    if C.dtype == torch.float32:
+        fusedmm_csr_f32(rowptr, colind, C, B, D, E, M, K, N, colind.numel(), stream)
+    else:
+        fusedmm_csr_bf16in_f32acc(rowptr, colind, C, B, D, E, M, K, N,
+                                  colind.numel(), stream)
     return E
 
 

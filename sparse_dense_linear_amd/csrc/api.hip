@@ -370,8 +370,8 @@ spmm_status_t run_with(int32_t dtype, const int32_t *rowptr,
                        const spmm_tuning_t *tuning, void *stream_ptr,
                        bool own_events, hipEvent_t e0, hipEvent_t e1,
                        bool vals_relative = false,
-                       const float *dot_rows = nullptr,
-                       const float *dot_cols = nullptr)
+                       const void *dot_rows = nullptr,
+                       const void *dot_cols = nullptr)
 {
     spmm_status_t st = check_args(dtype, rowptr, B, C, M, K, N);
     if (st != SPMM_SUCCESS)
@@ -609,6 +609,39 @@ spmm_status_t run_fusedmm(const int32_t *rowptr, const int32_t *colind,
     return st;
 }
 
+// FusedMM with bf16 C, B and D: the one-launch form only (fp32 values and
+// accumulation).  The two-launch route would need a product that weights
+// bf16 rows by fp32 values, which is not built.
+spmm_status_t run_fusedmm_bf16(const int32_t *rowptr, const int32_t *colind,
+                               const uint16_t *C, const uint16_t *B,
+                               const uint16_t *D, float *E, int64_t M, int64_t K,
+                               int64_t N, int64_t nnz, void *stream_ptr)
+{
+    g_last_error.clear();
+    if (M < 0 || K < 0 || N < 0 || nnz < 0)
+        return fail(SPMM_ERROR_INVALID_VALUE, "negative size");
+    if (M >= kMaxIndex || K >= kMaxIndex || N >= kMaxIndex || nnz >= kMaxIndex)
+        return fail(SPMM_ERROR_INVALID_VALUE, "M, K, N and nnz must be below 2^31");
+    if (M == 0 || N == 0)
+        return SPMM_SUCCESS;
+    if (rowptr == nullptr || E == nullptr || (nnz > 0 && (colind == nullptr ||
+        C == nullptr || B == nullptr || D == nullptr)))
+        return fail(SPMM_ERROR_INVALID_VALUE, "null pointer");
+    if ((((uintptr_t)C) | ((uintptr_t)B) | ((uintptr_t)D)) % 2 != 0 ||
+        ((uintptr_t)E) % 4 != 0)
+        return fail(SPMM_ERROR_INVALID_VALUE, "operand not aligned to its element size");
+    if (nnz == 0)  // E = 0: the product of an empty pattern (no operand read)
+        return run_with(SPMM_DTYPE_BF16, rowptr, colind, nullptr, nullptr, E, M, 0,
+                        N, nullptr, stream_ptr, false, nullptr, nullptr);
+    const WorkerConfig cfg = choose_worker(SPMM_DTYPE_BF16, N, D, E);
+    if (!fused_fits(cfg, N) || ((uintptr_t)C) % 16 != 0 || ((uintptr_t)B) % 16 != 0)
+        return fail(SPMM_ERROR_UNSUPPORTED,
+                    "bf16 FusedMM needs N a multiple of 8, at most 1024, and "
+                    "16-byte aligned C, B, D and E");
+    return run_with(SPMM_DTYPE_BF16, rowptr, colind, nullptr, D, E, M, K, N,
+                    nullptr, stream_ptr, false, nullptr, nullptr, false, C, B);
+}
+
 // The element-balanced product: one launch; carry slots in the stream's
 // work buffer, arrival counters in its plan scratch.
 spmm_status_t run_eb(int32_t dtype, const int32_t *rowptr, const int32_t *colind,
@@ -700,6 +733,15 @@ spmm_status_t fusedmm_csr_f32(const int32_t *rowptr, const int32_t *colind,
                               int64_t nnz, void *stream)
 {
     return run_fusedmm(rowptr, colind, C, B, D, E, M, K, N, nnz, stream);
+}
+
+spmm_status_t fusedmm_csr_bf16in_f32acc(const int32_t *rowptr,
+                                        const int32_t *colind, const uint16_t *C,
+                                        const uint16_t *B, const uint16_t *D,
+                                        float *E, int64_t M, int64_t K,
+                                        int64_t N, int64_t nnz, void *stream)
+{
+    return run_fusedmm_bf16(rowptr, colind, C, B, D, E, M, K, N, nnz, stream);
 }
 
 spmm_status_t sddmm_csr_f32(const int32_t *rowptr, const int32_t *colind,

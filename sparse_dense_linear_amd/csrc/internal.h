@@ -87,8 +87,9 @@ struct WorkerConfig {
 
 WorkerConfig choose_worker(int dtype, int64_t N, const void *B, const float *C);
 
-// Whether the FusedMM form of the worker covers cfg and N: fp32, 16-byte
-// vectors, and a whole row of N columns in one column pass.
+// Whether the FusedMM form of the worker covers cfg and N: 16-byte vectors
+// (4 fp32 or 8 bf16 elements) and a whole row of N <= 1024 columns in one
+// column pass.
 bool fused_fits(const WorkerConfig &cfg, int64_t N);
 
 struct WorkerArgs {
@@ -99,10 +100,10 @@ struct WorkerArgs {
     const void *B;         // FusedMM: D, the rows that the values weight
     float *C;              // null: plan only (no product)
     // FusedMM only (null otherwise): the value of an entry of row i at
-    // column j is <dot_rows_i, dot_cols_j>, both fp32 with N columns
-    // (dot_rows M x N, dot_cols K x N), and vals is not read.
-    const float *dot_rows;
-    const float *dot_cols;
+    // column j is <dot_rows_i, dot_cols_j>, both of B's element type with N
+    // columns (dot_rows M x N, dot_cols K x N), and vals is not read.
+    const void *dot_rows;
+    const void *dot_cols;
     int64_t M;
     int64_t K;
     int64_t N;

@@ -471,7 +471,7 @@ void call_kernel(WorkerArgs a, ProductShape ps)
         ysrc.base = (const char *)a.dot_cols;
         if constexpr (S::BUF)
             ysrc.rsrc = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<float *>(a.dot_cols), (short)0,
+                const_cast<void *>(a.dot_cols), (short)0,
                 (int)(uint32_t)(a.K * a.N * S::ESZ), kBufferWord3);
     }
 
@@ -645,7 +645,8 @@ hipError_t launch_dtype(const WorkerConfig &cfg, const WorkerArgs &a,
 
 bool fused_fits(const WorkerConfig &cfg, int64_t N)
 {
-    return cfg.dtype == SPMM_DTYPE_F32 && cfg.vec == 4 &&
+    // At most 1024 columns: wider bf16 rows (4 vectors per lane) spill.
+    return cfg.vec == (cfg.dtype == SPMM_DTYPE_F32 ? 4 : 8) && N <= 1024 &&
            N <= (int64_t)cfg.group * cfg.vec * cfg.nv;
 }
 
@@ -658,11 +659,14 @@ hipError_t launch_call(const WorkerConfig &cfg, const WorkerArgs &a,
     const uint64_t b_bytes = (uint64_t)a.K * (uint64_t)a.N * (uint64_t)esz;
     const bool buf = b_bytes < 0xFFFFFFFFull;
     if (a.dot_rows != nullptr) {
-        // FusedMM: fp32, 16-byte vectors, the whole row in one column pass.
+        // FusedMM: 16-byte vectors, the whole row in one column pass.
         if (!fused_fits(cfg, a.N) || a.dot_cols == nullptr)
             return hipErrorInvalidValue;
-        return buf ? launch_vec<SPMM_DTYPE_F32, 4, true, true>(cfg.group, cfg.nv, a, s, e0, e1)
-                   : launch_vec<SPMM_DTYPE_F32, 4, false, true>(cfg.group, cfg.nv, a, s, e0, e1);
+        if (cfg.dtype == SPMM_DTYPE_F32)
+            return buf ? launch_vec<SPMM_DTYPE_F32, 4, true, true>(cfg.group, cfg.nv, a, s, e0, e1)
+                       : launch_vec<SPMM_DTYPE_F32, 4, false, true>(cfg.group, cfg.nv, a, s, e0, e1);
+        return buf ? launch_vec<SPMM_DTYPE_BF16, 8, true, true>(cfg.group, cfg.nv, a, s, e0, e1)
+                   : launch_vec<SPMM_DTYPE_BF16, 8, false, true>(cfg.group, cfg.nv, a, s, e0, e1);
     }
     if (buf)
         return launch_dtype<true>(cfg, a, s, e0, e1);

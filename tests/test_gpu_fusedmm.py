@@ -168,3 +168,104 @@ def test_powerlaw_pattern():
     C = rng.standard_normal((p.M, p.N)).astype(np.float32)
     D = rng.standard_normal((p.K, p.N)).astype(np.float32)
     check(p.rowptr, p.colind, C, p.B.reshape(p.K, p.N), D, p.M, p.K, p.N, "powerlaw")
+
+
+# ---- bf16 inputs (one launch only) -------------------------------------
+
+def bf16(x):
+    """fp32 array -> bf16 bit patterns (uint16), round to nearest even."""
+    return W.f32_to_bf16_bits(np.ascontiguousarray(x, np.float32))
+
+
+def widen(bits):
+    """bf16 bit patterns -> the fp32 values they stand for (exact)."""
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _dev16(bits, shift=0):
+    flat = torch.from_numpy(np.ascontiguousarray(bits).reshape(-1).view(np.int16))
+    if not shift:
+        return flat.cuda()
+    buf = torch.zeros(flat.numel() + shift, dtype=torch.int16, device="cuda")
+    buf[shift:] = flat.cuda()
+    return buf[shift:]
+
+
+def run_fused_bf16(rowptr, colind, C, B, D, M, K, N, shift=0):
+    rp = torch.from_numpy(np.ascontiguousarray(rowptr, np.int32)).cuda()
+    ci = torch.from_numpy(np.ascontiguousarray(colind, np.int32)).cuda()
+    E = torch.full((M * N,), float("nan"), dtype=torch.float32, device="cuda")
+    nnz = int(rowptr[-1]) - int(rowptr[0])
+    sdl.fusedmm_csr_bf16in_f32acc(rp, ci, _dev16(C, shift), _dev16(B, shift), _dev16(D),
+                                  E, M, K, N, nnz)
+    torch.cuda.synchronize()
+    assert sdl.stream_faults() == 0
+    return E.cpu().numpy().reshape(M, N)
+
+
+def check_bf16(rowptr, colind, C, B, D, M, K, N, what=""):
+    """C, B, D are bf16 bits; the oracle gets the values they stand for, so
+    the fp32 bound applies unchanged (widening is exact)."""
+    E = run_fused_bf16(rowptr, colind, C, B, D, M, K, N)
+    Eref, T = oracle.fusedmm_ref(rowptr, colind, widen(C), widen(B), widen(D), N)
+    bad = ~(np.abs(E.astype(np.float64) - Eref) <= tol(N) * T + 1e-6)
+    if bad.any():
+        i, n = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {int(bad.sum())} of {E.size} outside the bound; "
+                             f"first ({i},{n}): gpu={E[i, n]!r} ref={Eref[i, n]!r} T={T[i, n]!r}")
+    return E
+
+
+def test_bf16_worked_example_bitwise():
+    """The worked example's values are exact in bf16 and every sum in it is
+    exact.  Padded with zero columns to N = 8 (the bf16 form needs N a
+    multiple of 8; zeros add nothing to a dot product), the bf16 call gives
+    the golden E in the first columns and zeros in the rest, bit for bit."""
+    g = json.load(open(os.path.join(GOLDEN, "worked_example_fig3_fig6.json")))
+    f = lambda k: np.array(g[k], np.float32)
+    N0, N = g["N"], 8
+    pad = lambda x: np.pad(x, ((0, 0), (0, N - N0)))
+    C, B, D = (pad(f(k)) for k in ("C", "B", "D"))
+    for x in (C, B, D):
+        assert np.array_equal(widen(bf16(x)), x)
+    E = run_fused_bf16(np.array(g["rowptr"]), np.array(g["colind"]), bf16(C),
+                       bf16(B), bf16(D), g["M"], g["K"], N)
+    assert np.array_equal(E[:, :N0], f("E"))
+    assert np.array_equal(E[:, N0:], np.zeros((g["M"], N - N0), np.float32))
+
+
+@pytest.mark.parametrize("N", [8, 16, 64, 128, 256, 512, 1024])
+def test_bf16_edge_rows(N):
+    rng = np.random.default_rng(N + 300)
+    M, K = 200, 4000
+    lengths = rng.choice(EDGE, size=M)
+    lengths[:len(EDGE)] = EDGE
+    rp, ci = pattern(lengths, K, seed=N + 300)
+    check_bf16(rp, ci, bf16(dense(rng, M, N)), bf16(dense(rng, K, N)),
+               bf16(dense(rng, K, N)), M, K, N, f"bf16 N={N}")
+
+
+def test_bf16_powerlaw_pattern():
+    p = W.make("powerlaw_262k_n64")
+    rng = np.random.default_rng(16)
+    C = bf16(rng.standard_normal((p.M, p.N)))
+    B = bf16(p.B.reshape(p.K, p.N))
+    D = bf16(rng.standard_normal((p.K, p.N)))
+    check_bf16(p.rowptr, p.colind, C, B, D, p.M, p.K, p.N, "bf16 powerlaw")
+
+
+def test_bf16_empty_and_unsupported():
+    rng = np.random.default_rng(17)
+    M, K = 40, 30
+    # no stored entries: E is zero
+    E = run_fused_bf16(np.zeros(M + 1, np.int32), np.zeros(0, np.int32),
+                       bf16(dense(rng, M, 16)), bf16(dense(rng, K, 16)),
+                       bf16(dense(rng, K, 16)), M, K, 16)
+    assert np.array_equal(E, np.zeros((M, 16), np.float32))
+    rp, ci = pattern(rng.integers(0, 5, M), K, seed=17)
+    # N not a multiple of 8, N above 1024, unaligned C and B: refused
+    for N, shift in [(12, 0), (1032, 0), (64, 1)]:
+        with pytest.raises(sdl.SpmmError) as e:
+            run_fused_bf16(rp, ci, bf16(dense(rng, M, N)), bf16(dense(rng, K, N)),
+                           bf16(dense(rng, K, N)), M, K, N, shift=shift)
+        assert e.value.status == 4, (N, shift)
