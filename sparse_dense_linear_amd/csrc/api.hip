@@ -527,10 +527,12 @@ spmm_status_t launch_sddmm_checked(int32_t dtype, const int32_t *rowptr,
     return SPMM_SUCCESS;
 }
 
-// FusedMM: E_i = sum_p <C_i, B_j> D_j.  The SDDMM values go to a
-// stream-ordered scratch array of nnz floats, which the product kernel
-// then reads as the values of A with D as its dense operand: two launches
-// on the stream, the values making one round trip through memory.
+// FusedMM: E_i = sum_p <C_i, B_j> D_j.  One launch of the product kernel
+// in its FusedMM form when the shape allows (each value formed where it is
+// used); otherwise the SDDMM values go to a stream-ordered scratch array of
+// nnz floats, which the product kernel then reads as the values of A with D
+// as its dense operand: two launches, the values making one round trip
+// through memory.
 spmm_status_t run_fusedmm(const int32_t *rowptr, const int32_t *colind,
                           const float *C, const float *B, const float *D,
                           float *E, int64_t M, int64_t K, int64_t N,

@@ -1,7 +1,9 @@
 // gather.h -- device building blocks shared by the product kernels: lane
 // groups and their column layout, exact loads of B vectors (fp32 or bf16),
 // the staged (column, value) entries, batches of U gathers issued without
-// branches, accumulation, row stores and the reduction across groups.
+// branches, accumulation, row stores and the reduction across groups, and
+// the FusedMM pieces (a group's dot product <X_i, Y_j> formed where the
+// value is used).
 // Included by worker.hip and eb.hip (each keeps its own copy: everything
 // here is in an anonymous namespace).
 #pragma once
@@ -258,24 +260,9 @@ __device__ inline void accumulate(const Batch<S> &bt, int u, bool on,
     axpy<S>(bt.buf[u], bt.v[u], on, acc);
 }
 
-// Group-local SAXPY over cnt staged entries: acc += val * B[col, cols of lane].
-template <class S>
-__device__ inline void consume(const Entry *st, int cnt, const BSrc &src,
-                               uint32_t row_bytes, const LaneCols<S> &lc,
-                               float (&acc)[S::NV][S::VEC])
-{
-    for (int u = 0; u < cnt; u += S::U) {
-        const int n = cnt - u < S::U ? cnt - u : S::U;
-        Batch<S> bt;
-        issue<S>(bt, st, u, n, src, row_bytes, lc);
-#pragma unroll
-        for (int x = 0; x < S::U; ++x)
-            accumulate<S>(bt, x, x < n, acc);
-    }
-}
-
-// As consume(), with entry k held in lane k's (col, val) instead of LDS
-// (read by lane shuffles).
+// Group-local SAXPY over entries first .. first+cnt-1 of a chunk held one
+// per lane (lane k: column `col`, value `val`), read by lane shuffles:
+// acc += val * B[col, this lane's columns], U gathers at a time.
 template <class S>
 __device__ inline void consume_lanes(int32_t col, float val, int first, int cnt,
                                      const BSrc &src, uint32_t row_bytes,

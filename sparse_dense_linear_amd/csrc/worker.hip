@@ -22,12 +22,14 @@
 //     the B/C columns (k*G + j)*VEC .. +VEC-1 for k < NV, so every gathered
 //     row of B is read, and every row of C written, as contiguous 16-byte
 //     vectors across the group.
-//   * colind/vals of the entries being worked on are staged in LDS, loaded
-//     once with coalesced loads and then read (as broadcasts) by the lanes
-//     that cover the N columns.
+//   * colind/vals of the entries being worked on are loaded once with
+//     coalesced loads, one entry per lane, and reach the lanes that cover
+//     the N columns from there: by lane shuffles for a medium row or chunk,
+//     through LDS (staged with their rows) for a short tile.
 //   * One launch per call: the first workgroups compute the plan
-//     (plan_device.h) while the others start on short tiles; three kinds
-//     of work item, all handled by one grid-stride loop:
+//     (plan_device.h) while the others start on short tiles; then every
+//     wavefront takes items from 64 work queues (see call_kernel).  Three
+//     kinds of work item:
 //       long chunk  (row, p0, p1) from the plan: the R groups split the
 //                   chunk's entries, their partial rows are summed by
 //                   butterfly shuffles, and group 0 adds the result to C
@@ -45,6 +47,9 @@
 //                   other two kinds.
 //   * Within an item, U gathers per lane are issued back to back before any
 //     of them is consumed.
+//   * FusedMM form (Shape::FUSED; [IntelMax] FusedMM operation, Fig. 6,
+//     Algorithm 3): the same items, with each entry's value formed by its
+//     lane group as <X_i, Y_j> where it is used instead of read from vals.
 #include <hip/hip_ext.h>
 
 #include "gather.h"
