@@ -30,7 +30,7 @@ def test_header_declares_entry_points():
                  "spmm_resolve_tuning", "spmm_plan_export", "spmm_status_string",
                  "spmm_last_error", "spmm_timing_enable", "spmm_timing_read",
                  "spmm_stream_faults", "sddmm_csr_f32", "sddmm_csr_bf16in_f32acc",
-                 "fusedmm_csr_f32"):
+                 "fusedmm_csr_f32", "fusedmm_csr_bf16in_f32acc"):
         assert must in names
 
 
@@ -204,6 +204,29 @@ def test_fusedmm_host_validation(M, K, N, nnz, rowptr, E, D, expect):
     assert rc == expect, sdl.lib().spmm_last_error()
 
 
+@pytest.mark.parametrize("M,K,N,nnz,rowptr,C,D,E,expect", [
+    (-1, 4, 8, 4, FAKE, FAKE, FAKE, FAKE, 1),        # negative M
+    (4, 4, 8, 2 ** 31, FAKE, FAKE, FAKE, FAKE, 1),   # nnz too large
+    (4, 4, 8, 3, None, FAKE, FAKE, FAKE, 1),         # rowptr null
+    (4, 4, 8, 3, FAKE, None, FAKE, FAKE, 1),         # C null with entries
+    (4, 4, 8, 3, FAKE, FAKE, None, FAKE, 1),         # D null with entries
+    (4, 4, 8, 3, FAKE, FAKE, FAKE, None, 1),         # E null
+    (4, 4, 8, 3, FAKE, FAKE + 1, FAKE, FAKE, 1),     # C not 2-byte aligned
+    (4, 4, 8, 3, FAKE, FAKE, FAKE, FAKE + 2, 1),     # E not 4-byte aligned
+    (4, 4, 12, 3, FAKE, FAKE, FAKE, FAKE, 4),        # N not a multiple of 8
+    (4, 4, 1032, 3, FAKE, FAKE, FAKE, FAKE, 4),      # N above 1024
+    (4, 4, 64, 3, FAKE, FAKE + 2, FAKE, FAKE, 4),    # C not 16-byte aligned
+    (0, 4, 8, 0, None, None, None, None, 0),         # M == 0: nothing to do
+    (4, 4, 0, 0, None, None, None, None, 0),         # N == 0: nothing to do
+])
+def test_fusedmm_bf16_host_validation(M, K, N, nnz, rowptr, C, D, E, expect):
+    """bf16 FusedMM refuses bad arguments, and shapes its one launch does not
+    cover, on the host before any HIP call."""
+    rc = raw_call("fusedmm_csr_bf16in_f32acc", rowptr, FAKE, C, FAKE, D, E, M, K, N,
+                  nnz, None)
+    assert rc == expect, sdl.lib().spmm_last_error()
+
+
 def test_fusedmm_forced_allocation_failure(monkeypatch):
     monkeypatch.setenv("SPMM_TEST_FAIL_ALLOC", "1")
     rc = raw_call("fusedmm_csr_f32", FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 4, 3, None)
@@ -218,3 +241,6 @@ def test_sddmm_binding_checks_operands():
         sdl.sddmm_csr_f32(t, t, f, f, f, 3, 2, 2)
     with pytest.raises((ValueError, TypeError)):
         sdl.fusedmm_csr_f32(t, t, f, f, f, f, 3, 2, 2, 4)
+    h = torch.zeros(4, dtype=torch.int16)
+    with pytest.raises((ValueError, TypeError)):
+        sdl.fusedmm_csr_bf16in_f32acc(t, t, h, h, h, f, 3, 2, 2, 4)
