@@ -57,7 +57,8 @@ def test_worked_example_bitwise(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [1, 3, 4, 8, 32, 33, 64, 100, 128, 256, 512, 1000])
+@pytest.mark.parametrize("N", [1, 3, 4, 8, 32, 33, 64, 100, 128, 256, 512, 1000,
+                               1025, 2304])
 def test_edge_rows(N, dtype):
     check(edge_problem(N, dtype), f"N={N} {dtype}")
 

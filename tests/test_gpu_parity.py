@@ -53,11 +53,14 @@ def test_worked_example_bitwise():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [1, 3, 4, 8, 32, 33, 64, 100, 128, 256, 512, 1000])
+@pytest.mark.parametrize("N", [1, 3, 4, 8, 32, 33, 64, 100, 128, 256, 512, 1000,
+                               1025, 1500, 2304])
 def test_edge_rows_all_paths(N, dtype):
     """Rows of every length class (empty, short, medium, long with many
     chunks) for many N, including N that are not multiples of the lane
-    vector and N above one column pass."""
+    vector and N that take several column passes (1025: 5 passes of 256
+    single-element columns in fp32; 1500 and 2304: 2-3 passes of 16-byte
+    vectors, the last one partial)."""
     p = edge_problem(N, dtype, seed=N)
     C = run_gpu(p)
     Cref, Sref = reference(p)
