@@ -64,3 +64,29 @@ def test_B_above_4GiB(kernel):
     del B
     Cref, Sref = oracle.spmm_ref(rowptr, compact.astype(np.int32), vals, B_used, N)
     assert_parity(C.cpu().numpy().reshape(M, N), Cref, Sref, "f32", f"B > 4 GiB, {kernel}")
+
+
+def test_fusedmm_B_above_4GiB():
+    """FusedMM's one-launch form through flat addresses: B (and D, the same
+    array here) above 4 GiB."""
+    rowptr, colind, _ = _problem(seed=13)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(14)
+    B = torch.randn(K * N, generator=g, device="cuda")
+    Cd = torch.randn(M * N, generator=g, device="cuda")
+    E = torch.full((M * N,), float("nan"), device="cuda")
+    rp = torch.from_numpy(rowptr).cuda()
+    ci = torch.from_numpy(colind).cuda()
+    sdl.fusedmm_csr_f32(rp, ci, Cd, B, B, E, M, K, N, colind.size)
+    torch.cuda.synchronize()
+    assert sdl.stream_faults() == 0
+
+    used, compact = np.unique(colind, return_inverse=True)
+    B_used = B.view(K, N)[torch.from_numpy(used).cuda().long()].cpu().numpy()
+    del B
+    C_host = Cd.cpu().numpy().reshape(M, N)
+    Eref, T = oracle.fusedmm_ref(rowptr, compact.astype(np.int32), C_host, B_used, B_used, N)
+    got = E.cpu().numpy().reshape(M, N).astype(np.float64)
+    tol = 2 * max(1e-5, N * 2.0 ** -23)   # the FusedMM bound of test_gpu_fusedmm
+    bad = ~(np.abs(got - Eref) <= tol * T + 1e-6)
+    assert not bad.any(), f"{int(bad.sum())} of {got.size} outside the bound"
