@@ -705,6 +705,7 @@ spmm_status_t run_eb(int32_t dtype, const int32_t *rowptr, const int32_t *colind
     a.waves = waves;
     a.carry_val = (float *)mem;
     a.arrive = carve((char *)scratch, lay).medium_rows;
+    a.queues = carve((char *)scratch, lay).queues;
     a.epoch = epoch;
     const WorkerConfig cfg = choose_worker(dtype, N, B, C);
     err = launch_eb(cfg, a, stream, tc.work0, tc.work1);

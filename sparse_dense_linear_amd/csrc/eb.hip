@@ -173,6 +173,13 @@ void eb_kernel(EbArgs a)
     const int g = lane / S::G;
     const int j = lane % S::G;
     const int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + wid;
+    // Every call on a stream takes the next epoch, and a planned product
+    // call draws from the queue counter set of its epoch's parity, which the
+    // call before it must clear: this call clears the set of epoch + 1 (no
+    // call on the stream is using it now).
+    if (w == 0)
+        for (int q = lane; q < kQueues; q += kWave)
+            a.queues[(((a.epoch + 1) & 1) * kQueues + q) * kQueueStride] = 0;
     if (w >= a.waves)
         return;
     const int32_t *rowptr = a.rowptr;

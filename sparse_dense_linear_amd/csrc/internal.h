@@ -59,9 +59,10 @@ struct PlanBuffers {
     uint64_t *chunk_row;     // [chunk_cap] row of each chunk
     uint64_t *chunk_k;       // [chunk_cap] position of the chunk in its row
     uint32_t *faults;        // items the product gave up waiting for (not tagged)
-    uint32_t *queues;        // [2][kQueues * kQueueStride] grab counters: a call
-                             // uses set epoch & 1 and clears the other set for
-                             // the next call (not tagged)
+    uint32_t *queues;        // [2][kQueues * kQueueStride] grab counters: a
+                             // product call uses set epoch & 1; every call that
+                             // takes an epoch (product or element-balanced)
+                             // clears set (epoch + 1) & 1 (not tagged)
     int64_t chunk_cap;       // M + kChunkTableSlack
 };
 
@@ -151,6 +152,8 @@ struct EbArgs {
     int64_t waves;        // spans (wavefronts) of the launch
     float *carry_val;     // [2 * waves * N] partial rows: head and tail slot
     uint64_t *arrive;     // [waves] arrival counters, tagged with epoch
+    uint32_t *queues;     // the stream's product queue counters: this call
+                          // clears the set of epoch + 1 (PlanBuffers::queues)
     uint32_t epoch;       // this call's epoch (words with another tag are 0)
 };
 

@@ -451,8 +451,10 @@ void call_kernel(WorkerArgs a, ProductShape ps)
             pc.lane = lane;
             plan_block(pc, blockIdx.x, wid, lds.plan);
         }
-        // Clear the queue counters of the next call on this stream (the
-        // previous call, which used them, has ended).
+        // Clear the queue counters of the next epoch on this stream (the
+        // call before this one, which used them, has ended).  Every call
+        // that takes an epoch does this, the element-balanced kernel too, so
+        // a product call always finds its set cleared.
         if (blockIdx.x == 0 && wid == 0)
             for (int q = lane; q < kQueues; q += kWave)
                 a.plan.queues[((a.epoch + 1) & 1) * kQueues * kQueueStride +

@@ -1,0 +1,100 @@
+"""Calls on several streams.  Each stream has its own scratch (plan words,
+queue counters, epochs) and its own FusedMM / element-balanced work buffer,
+so calls on two streams may run at the same time; calls on one stream reuse
+its scratch, call after call.  Every result is checked against the oracle.
+Streams are created with torch's default priority."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_dense_linear_amd as sdl
+import workloads as W
+from gpu_helpers import assert_parity
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _dev(p):
+    return (torch.from_numpy(p.rowptr).cuda(), torch.from_numpy(p.colind).cuda(),
+            torch.from_numpy(p.vals).cuda(),
+            torch.from_numpy(np.ascontiguousarray(p.B).reshape(-1)).cuda())
+
+
+def test_two_streams_concurrently():
+    """Two problems of different shapes, product and element-balanced kernel,
+    issued alternately on two streams several times (so the streams' calls
+    overlap and each stream's epochs and queue sets advance), then checked."""
+    p1 = W.powerlaw_rows(M=50000, N=64, seed=31)
+    p2 = W.rows_with_lengths(np.random.default_rng(32).integers(0, 300, 3000), 5000, 128,
+                             seed=32)
+    a1, a2 = _dev(p1), _dev(p2)
+    C1 = torch.full((p1.M * p1.N,), float("nan"), device="cuda")
+    C2 = torch.full((p2.M * p2.N,), float("nan"), device="cuda")
+    E1 = torch.full_like(C1, float("nan"))
+    E2 = torch.full_like(C2, float("nan"))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(5):
+        with torch.cuda.stream(s1):
+            sdl.spmm_csr_f32(*a1, C1, p1.M, p1.K, p1.N, stream=s1)
+            sdl.spmm_csr_eb(sdl.DTYPE_F32, *a1, E1, p1.M, p1.K, p1.N, stream=s1)
+        with torch.cuda.stream(s2):
+            sdl.spmm_csr_f32(*a2, C2, p2.M, p2.K, p2.N, stream=s2)
+            sdl.spmm_csr_eb(sdl.DTYPE_F32, *a2, E2, p2.M, p2.K, p2.N, stream=s2)
+    torch.cuda.synchronize()
+    assert sdl.stream_faults(s1) == 0 and sdl.stream_faults(s2) == 0
+    for p, C, E, what in ((p1, C1, E1, "stream 1"), (p2, C2, E2, "stream 2")):
+        Cref, Sref = oracle.spmm_ref(p.rowptr, p.colind, p.vals, p.B, p.N)
+        assert_parity(C.cpu().numpy().reshape(p.M, p.N), Cref, Sref, "f32", what)
+        assert_parity(E.cpu().numpy().reshape(p.M, p.N), Cref, Sref, "f32", what + " eb")
+
+
+def test_fusedmm_on_two_streams():
+    """The two-launch FusedMM route keeps its value array per stream: two
+    calls in flight on two streams must not share it."""
+    rng = np.random.default_rng(33)
+    M, K, N = 4000, 3000, 6            # N = 6: the two-launch route
+    out = []
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    cases = []
+    for s in streams:
+        p = W.rows_with_lengths(rng.integers(0, 60, M), K, N, seed=int(rng.integers(1 << 30)))
+        Cd = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+        D = rng.uniform(-1, 1, (K, N)).astype(np.float32)
+        E = torch.full((M * N,), float("nan"), device="cuda")
+        cases.append((p, Cd, D, E, s))
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for p, Cd, D, E, s in cases:
+            with torch.cuda.stream(s):
+                sdl.fusedmm_csr_f32(torch.from_numpy(p.rowptr).cuda(),
+                                    torch.from_numpy(p.colind).cuda(),
+                                    torch.from_numpy(Cd).cuda(),
+                                    torch.from_numpy(p.B.reshape(K, N)).cuda(),
+                                    torch.from_numpy(D).cuda(), E, M, K, N, p.nnz, stream=s)
+    torch.cuda.synchronize()
+    for p, Cd, D, E, s in cases:
+        assert sdl.stream_faults(s) == 0
+        Eref, T = oracle.fusedmm_ref(p.rowptr, p.colind, Cd, p.B.reshape(K, N), D, N)
+        got = E.cpu().numpy().reshape(M, N).astype(np.float64)
+        bad = ~(np.abs(got - Eref) <= 2 * max(1e-5, N * 2.0 ** -23) * T + 1e-6)
+        assert not bad.any(), f"{int(bad.sum())} of {got.size} outside the bound"
+
+
+def test_growing_and_shrinking_calls_on_one_stream():
+    """Calls of increasing then decreasing size on one stream: the stream's
+    scratch grows when a call needs more, and later smaller calls reuse it."""
+    s = torch.cuda.Stream()
+    for M in (1000, 120000, 3000, 60000):
+        p = W.powerlaw_rows(M=M, N=32, seed=M)
+        a = _dev(p)
+        C = torch.full((p.M * p.N,), float("nan"), device="cuda")
+        with torch.cuda.stream(s):
+            sdl.spmm_csr_f32(*a, C, p.M, p.K, p.N, stream=s)
+        s.synchronize()
+        assert sdl.stream_faults(s) == 0
+        rows = np.random.default_rng(M).choice(p.M, 500, replace=False)
+        Cref, Sref = oracle.spmm_ref(p.rowptr, p.colind, p.vals, p.B, p.N, rows=rows)
+        assert_parity(C.cpu().numpy().reshape(p.M, p.N)[rows], Cref, Sref, "f32", f"M={M}")
