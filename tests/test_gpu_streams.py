@@ -56,7 +56,6 @@ def test_fusedmm_on_two_streams():
     calls in flight on two streams must not share it."""
     rng = np.random.default_rng(33)
     M, K, N = 4000, 3000, 6            # N = 6: the two-launch route
-    out = []
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     cases = []
     for s in streams:
@@ -98,3 +97,53 @@ def test_growing_and_shrinking_calls_on_one_stream():
         rows = np.random.default_rng(M).choice(p.M, 500, replace=False)
         Cref, Sref = oracle.spmm_ref(p.rowptr, p.colind, p.vals, p.B, p.N, rows=rows)
         assert_parity(C.cpu().numpy().reshape(p.M, p.N)[rows], Cref, Sref, "f32", f"M={M}")
+
+
+def test_every_kind_of_call_interleaved_on_one_stream():
+    """Product, element-balanced product, FusedMM (one launch and two
+    launches), SDDMM and a product of another width, one after another on
+    one stream, twice: each call takes the stream's next epoch and reuses its
+    scratch and work buffer; every result must still match the oracle."""
+    rng = np.random.default_rng(41)
+    s = torch.cuda.Stream()
+    p = W.powerlaw_rows(M=30000, N=64, seed=41)
+    q = W.rows_with_lengths(rng.integers(0, 200, 2500), 4000, 6, seed=42)   # N = 6
+    rp, ci, v, B = _dev(p)
+    rq, cq, vq, Bq = _dev(q)
+    Cf = rng.uniform(-1, 1, (p.M, p.N)).astype(np.float32)
+    Df = rng.uniform(-1, 1, (p.K, p.N)).astype(np.float32)
+    Cq = rng.uniform(-1, 1, (q.M, q.N)).astype(np.float32)
+    Dq = rng.uniform(-1, 1, (q.K, q.N)).astype(np.float32)
+    Cf_d, Df_d = torch.from_numpy(Cf).cuda(), torch.from_numpy(Df).cuda()
+    Cq_d, Dq_d = torch.from_numpy(Cq).cuda(), torch.from_numpy(Dq).cuda()
+    nan = lambda n: torch.full((n,), float("nan"), device="cuda")
+    outs = {k: nan(n) for k, n in [("spmm", p.M * p.N), ("eb", p.M * p.N),
+                                   ("fused1", p.M * p.N), ("fused2", q.M * q.N),
+                                   ("sddmm", p.nnz), ("spmm_q", q.M * q.N)]}
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            sdl.spmm_csr_f32(rp, ci, v, B, outs["spmm"], p.M, p.K, p.N, stream=s)
+            sdl.spmm_csr_eb(sdl.DTYPE_F32, rp, ci, v, B, outs["eb"], p.M, p.K, p.N, stream=s)
+            sdl.fusedmm_csr_f32(rp, ci, Cf_d, B, Df_d, outs["fused1"], p.M, p.K, p.N,
+                                p.nnz, stream=s)
+            sdl.fusedmm_csr_f32(rq, cq, Cq_d, Bq, Dq_d, outs["fused2"], q.M, q.K, q.N,
+                                q.nnz, stream=s)
+            sdl.sddmm_csr_f32(rp, ci, Cf_d, B, outs["sddmm"], p.M, p.K, p.N, stream=s)
+            sdl.spmm_csr_f32(rq, cq, vq, Bq, outs["spmm_q"], q.M, q.K, q.N, stream=s)
+    torch.cuda.synchronize()
+    assert sdl.stream_faults(s) == 0
+    got = {k: t.cpu().numpy() for k, t in outs.items()}
+    Cref, Sref = oracle.spmm_ref(p.rowptr, p.colind, p.vals, p.B, p.N)
+    assert_parity(got["spmm"].reshape(p.M, p.N), Cref, Sref, "f32", "spmm")
+    assert_parity(got["eb"].reshape(p.M, p.N), Cref, Sref, "f32", "eb")
+    Cqr, Sqr = oracle.spmm_ref(q.rowptr, q.colind, q.vals, q.B, q.N)
+    assert_parity(got["spmm_q"].reshape(q.M, q.N), Cqr, Sqr, "f32", "spmm N=6")
+    tol = lambda n: 2 * max(1e-5, n * 2.0 ** -23)
+    for key, r, Cx, Dx in (("fused1", p, Cf, Df), ("fused2", q, Cq, Dq)):
+        Eref, T = oracle.fusedmm_ref(r.rowptr, r.colind, Cx, r.B.reshape(r.K, r.N), Dx, r.N)
+        e = got[key].reshape(r.M, r.N).astype(np.float64)
+        assert np.all(np.abs(e - Eref) <= tol(r.N) * T + 1e-6), key
+    Aref, S = oracle.sddmm_ref(p.rowptr, p.colind, Cf, p.B.reshape(p.K, p.N), p.N)
+    assert np.all(np.abs(got["sddmm"].astype(np.float64) - Aref) <=
+                  max(1e-5, p.N * 2.0 ** -23) * S + 1e-6), "sddmm"
