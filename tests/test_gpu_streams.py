@@ -147,3 +147,43 @@ def test_every_kind_of_call_interleaved_on_one_stream():
     Aref, S = oracle.sddmm_ref(p.rowptr, p.colind, Cf, p.B.reshape(p.K, p.N), p.N)
     assert np.all(np.abs(got["sddmm"].astype(np.float64) - Aref) <=
                   max(1e-5, p.N * 2.0 ** -23) * S + 1e-6), "sddmm"
+
+
+def test_host_threads_on_their_own_streams():
+    """Four host threads, each with its own stream, call the library at the
+    same time (the binding releases Python's lock during a call), so the
+    per-stream tables of scratch and work buffers are created and looked up
+    concurrently."""
+    import threading
+
+    problems = [W.powerlaw_rows(M=20000, N=64, seed=50 + t) for t in range(4)]
+    results, errors = {}, []
+
+    def work(t):
+        try:
+            p = problems[t]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                a = _dev(p)
+                C = torch.full((p.M * p.N,), float("nan"), device="cuda")
+                E = torch.full((p.M * p.N,), float("nan"), device="cuda")
+                for _ in range(10):
+                    sdl.spmm_csr_f32(*a, C, p.M, p.K, p.N, stream=s)
+                    sdl.spmm_csr_eb(sdl.DTYPE_F32, *a, E, p.M, p.K, p.N, stream=s)
+            s.synchronize()
+            results[t] = (C.cpu().numpy(), E.cpu().numpy(), sdl.stream_faults(s))
+        except Exception as exc:           # reported by the main thread
+            errors.append(exc)
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not errors, errors
+    for t, p in enumerate(problems):
+        C, E, faults = results[t]
+        assert faults == 0
+        Cref, Sref = oracle.spmm_ref(p.rowptr, p.colind, p.vals, p.B, p.N)
+        assert_parity(C.reshape(p.M, p.N), Cref, Sref, "f32", f"thread {t}")
+        assert_parity(E.reshape(p.M, p.N), Cref, Sref, "f32", f"thread {t} eb")
