@@ -32,6 +32,9 @@
  * Asynchrony: a call only enqueues work on `stream` (a hipStream_t; NULL is
  * the null stream) and returns; it never waits for the device.  Inputs must
  * stay alive, and C must not be read, until the stream has passed the call.
+ * Calls may come from several host threads at once; calls on different
+ * streams may run on the device at the same time (each stream has its own
+ * scratch), and calls on one stream run one after another.
  *
  * Errors: every call returns a status; nothing throws across the ABI.
  * Argument errors are found on the host before any HIP call.  The contents
