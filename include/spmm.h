@@ -27,7 +27,10 @@
  * Ownership and memory: every pointer is device memory owned by the caller;
  * the library never frees or retains it.  The library allocates its own
  * scratch space (the row plan) from a stream-ordered pool per device, so
- * calls on different streams do not share scratch.
+ * calls on different streams do not share scratch.  It keeps one scratch
+ * block (and, for FusedMM's two-launch route and the element-balanced
+ * kernel, one work buffer) per stream it has been called on, grown when a
+ * call needs more, until the process ends.
  *
  * Asynchrony: a call only enqueues work on `stream` (a hipStream_t; NULL is
  * the null stream) and returns; it never waits for the device.  Inputs must
