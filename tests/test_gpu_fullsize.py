@@ -1,8 +1,10 @@
 """Full-size workloads on the GPU, in the launch configuration the benchmark
-times (the plain entry points with default thresholds).  Small workloads are
-compared element by element; the two large ones on sampled rows that the
-oracle computes one by one (every hub row of the skewed matrix is too
-expensive; a sample of hubs is included)."""
+times (the plain entry points with default thresholds), compared with the
+fp64 oracle on every element.  The two large workloads are compared in
+blocks of consecutive rows (the oracle computes one block at a time, so the
+reference never needs to hold all of C in fp64), every hub row of the
+skewed matrix included.  Their plans are compared bit for bit with the plan
+oracle as well."""
 import sys
 import time
 
@@ -10,6 +12,8 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
+import sparse_dense_linear_amd as sdl
 import workloads as W
 from gpu_helpers import assert_parity, reference, run_gpu
 
@@ -34,20 +38,43 @@ def test_full_compare(name):
     log(f"{name}: all {C.size} elements within bound, worst err/S {worst:.2e}")
 
 
+# Rows per oracle block: about 2^25 elements of C (two fp64 arrays of
+# 256 MiB for the reference and its bound).
+BLOCK_ELEMS = 1 << 25
+
+
 @pytest.mark.parametrize("name", ["banded_4m_n128", "skew_1m_n512_bf16"])
-def test_full_sampled(name):
+def test_full_streamed(name):
+    """The plan of the full matrix (default thresholds) equals the plan
+    oracle bit for bit, and every element of C matches the oracle, compared
+    one block of consecutive rows at a time."""
     t = time.time()
     p = W.make(name)
     log(f"{name}: generated nnz={p.nnz} in {time.time() - t:.1f}s")
+
+    dt = 0 if p.dtype == "f32" else 1
+    tun = sdl.resolve_tuning(dt, p.N)
+    got = sdl.plan_export(torch.from_numpy(p.rowptr).cuda(), tun)
+    want = oracle.plan_ref(p.rowptr, tun.short_max, tun.medium_max, tun.chunk_nnz)
+    for k in ("n_short", "n_medium", "n_long", "n_chunks"):
+        assert got[k] == want[k], k
+    assert np.array_equal(got["medium_rows"], want["medium_rows"])
+    assert np.array_equal(got["long_rows"], want["long_rows"])
+    assert np.array_equal(got["chunks"], want["chunks"])
+    log(f"{name}: plan equal ({got['n_medium']} medium, {got['n_long']} long, "
+        f"{got['n_chunks']} chunks)")
+    del got, want
+
     C = run_gpu(p, fill=float("nan"))
-    # every element must have been written
-    assert not np.isnan(C).any(), "unwritten (NaN) elements in C"
-    rng = np.random.default_rng(0)
-    rows = np.concatenate([np.arange(64), np.arange(p.M - 64, p.M),
-                           rng.choice(p.M, 4096, replace=False)])
-    if "hubs" in p.meta:
-        rows = np.concatenate([rows, rng.choice(p.meta["hubs"], 12, replace=False)])
-    rows = np.unique(rows)
-    Cref, Sref = reference(p, rows=rows)
-    worst = assert_parity(C[rows], Cref, Sref, p.dtype, name)
-    log(f"{name}: {rows.size} sampled rows within bound, worst err/S {worst:.2e}")
+    rows_per_block = max(1, BLOCK_ELEMS // p.N)
+    worst = 0.0
+    t = time.time()
+    for r0 in range(0, p.M, rows_per_block):
+        rows = np.arange(r0, min(p.M, r0 + rows_per_block), dtype=np.int64)
+        Cref, Sref = reference(p, rows=rows)
+        w = assert_parity(C[rows[0]:rows[-1] + 1], Cref, Sref, p.dtype,
+                          f"{name} rows {rows[0]}..{rows[-1]}")
+        worst = max(worst, w)
+        del Cref, Sref
+    log(f"{name}: all {p.M} rows ({C.size} elements) within bound in "
+        f"{time.time() - t:.1f}s, worst err/S {worst:.2e}")
