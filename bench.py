@@ -18,10 +18,14 @@ Besides the headline, the line carries
                 measured by rocprofv3 counters (FETCH_SIZE + WRITE_SIZE,
                 scaled by a copy kernel of known size) when the committed
                 profile matches the current kernel sources, else null;
-  cold          median and best of 20 event-timed calls, each after a 1 GiB
-                write that evicts L2 and the Infinity Cache;
+                `cold_achieved` / `cold_frac`: the same for the median of
+                the cold calls;
+  cold          median and best of 20 calls, each after a 1 GiB write that
+                evicts L2 and the Infinity Cache, each launch timed by the
+                library's events;
   cpu_baseline  the fp64 oracle timed on this host's cores on the same
-                matrix (a reported baseline, not a target).
+                matrix, and on one core, with the CPU model (a reported
+                baseline, not a target).
 """
 from __future__ import annotations
 
@@ -41,6 +45,13 @@ METRIC = ("SpMM GFLOP/s (2·nnz·N) and effective HBM GB/s as % of peak, "
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "powerlaw_262k_n64"
 KERNEL_SOURCES = ["sparse_dense_linear_amd/csrc/worker.hip",
+                  "sparse_dense_linear_amd/csrc/worker_impl.h",
+                  "sparse_dense_linear_amd/csrc/worker_f32_buf.hip",
+                  "sparse_dense_linear_amd/csrc/worker_f32_flat.hip",
+                  "sparse_dense_linear_amd/csrc/worker_bf16_buf.hip",
+                  "sparse_dense_linear_amd/csrc/worker_bf16_flat.hip",
+                  "sparse_dense_linear_amd/csrc/worker_fused_buf.hip",
+                  "sparse_dense_linear_amd/csrc/worker_fused_flat.hip",
                   "sparse_dense_linear_amd/csrc/eb.hip",
                   "sparse_dense_linear_amd/csrc/gather.h",
                   "sparse_dense_linear_amd/csrc/span.h",
@@ -91,26 +102,55 @@ def measured_traffic(workload: str, op: str = "spmm"):
     return float(m_b.group(1))
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(p, budget_s: float = 10.0, op: str = "spmm", dense=None) -> dict:
+    """The fp64 oracle on this host: on all cores (the reported value) and on
+    one core, each repeated for about budget_s seconds on the whole
+    matrix (at least once)."""
     import oracle
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        if op in ("spmm", "eb"):
-            oracle.spmm_ref(p.rowptr, p.colind, p.vals, p.B, p.N, with_bound=False)
-        elif op == "sddmm":
-            oracle.sddmm_ref(p.rowptr, p.colind, dense, p.B, p.N)
-        else:
-            oracle.fusedmm_ref(p.rowptr, p.colind, dense, p.B, p.B, p.N)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 1000:
-            break
+
+    def leg(threads):
+        oracle.set_num_threads(threads)
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            if op in ("spmm", "eb"):
+                oracle.spmm_ref(p.rowptr, p.colind, p.vals, p.B, p.N, with_bound=False)
+            elif op == "sddmm":
+                oracle.sddmm_ref(p.rowptr, p.colind, dense, p.B, p.N)
+            else:
+                oracle.fusedmm_ref(p.rowptr, p.colind, dense, p.B, p.B, p.N)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 1000:
+                return reps, el
+
     op_flops = flops(p) * (2 if op == "fusedmm" else 1)
+    what = {"spmm": "C only, no bound", "eb": "C only, no bound",
+            "sddmm": "SDDMM values and bound", "fusedmm": "FusedMM rows and bound"}[op]
+    cores = oracle.num_threads()  # OpenMP's default: the host's threads
+    reps, el = leg(cores)
+    reps1, el1 = leg(1)
+    oracle.set_num_threads(cores)
     return {"value": round(op_flops * reps / el / 1e9, 4), "unit": "GFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"the whole {p.name} matrix ({ {'spmm': 'C only, no bound', 'eb': 'C only, no bound', 'sddmm': 'SDDMM values and bound', 'fusedmm': 'FusedMM rows and bound'}[op]}), "
-                      f"{reps} repetitions in {el:.1f} s"}
+            "cores": cores, "kind": "oracle",
+            "sample": f"the whole {p.name} matrix ({what}), {reps} repetitions "
+                      f"in {el:.1f} s on {cores} threads",
+            "one_core": {"value": round(op_flops * reps1 / el1 / 1e9, 4),
+                         "unit": "GFLOP/s", "cores": 1,
+                         "sample": f"{reps1} repetitions in {el1:.1f} s"},
+            "cpu_model": cpu_model()}
 
 
 def gather_ceiling(torch, dev) -> dict:
@@ -304,20 +344,26 @@ def main() -> int:
     worker_avg_ms = worker_ms / max(ncalls, 1)
     achieved = mb / (worker_avg_ms * 1e-3) / 1e9 if worker_avg_ms > 0 else None
 
-    # cold calls: evict L2 and the Infinity Cache before each call
+    # cold calls: evict L2 and the Infinity Cache (a 1 GiB write on the same
+    # stream) before each call; each call's launch is timed by the events
+    # the library attaches to it
     evict = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     cold = []
     for _ in range(args.cold_reps):
         evict.fill_(1.0)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        sdl.timing_enable(True)
         step()
-        e1.record(stream)
-        e1.synchronize()
-        cold.append(e0.elapsed_time(e1))
+        sdl.timing_enable(False)
+        _, ms, n = sdl.timing_read()
+        if n != 1:
+            raise RuntimeError(f"expected one timed launch per cold call, got {n}")
+        cold.append(ms)
     del evict
+    if sdl.stream_faults(stream):
+        raise RuntimeError("items were left undone in the cold calls")
     cold_med = float(np.median(cold)) if cold else None
+    cold_best = min(cold) if cold else None
+    cold_ach = None if not cold_med else mb / (cold_med * 1e-3) / 1e9
 
     out = {
         "metric": METRIC if args.op in ("spmm", "eb") else METRIC.replace(
@@ -349,8 +395,12 @@ def main() -> int:
             "unit": "GB/s",
             "frac": None if achieved is None else round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(p.name, args.op),
+            # the same launch after a 1 GiB eviction of L2 and the Infinity
+            # Cache (median of the cold calls below)
+            "cold_achieved": None if cold_ach is None else round(cold_ach, 2),
+            "cold_frac": None if cold_ach is None else round(cold_ach / HBM_PEAK_GBPS, 4),
         },
-        "cold": {"median_ms": cold_med, "best_ms": min(cold) if cold else None,
+        "cold": {"median_ms": cold_med, "best_ms": cold_best,
                  "reps": len(cold),
                  "eff_GBps_median": None if not cold_med else round(mb / (cold_med * 1e-3) / 1e9, 2),
                  "gflops_median": None if not cold_med else round(op_flops / (cold_med * 1e-3) / 1e9, 3)},

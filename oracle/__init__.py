@@ -86,6 +86,8 @@ def load_library(path: str):
     ]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
+    lib.oracle_set_num_threads.restype = None
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     return lib
 
 
@@ -207,6 +209,12 @@ def fusedmm_ref(rowptr, colind, C, B, D, N: int, rows=None, library=None):
 def num_threads() -> int:
     """Threads the oracle's row loop uses (OpenMP)."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for later oracle calls' row loop (the results do not depend
+    on it; used to time the oracle on one core)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def _kind_of(arr: np.ndarray) -> int:

@@ -71,6 +71,18 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Threads of later calls' row loop (n >= 1); the arithmetic of a row does
+ * not depend on it.  Used to time the oracle on one core. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /*
  * One output row, [IntelMax] Algorithm 2: loop over the non-zeros of row i;
  * fetch the value s and the column k; add s * B_k into the accumulator row.
