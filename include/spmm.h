@@ -29,15 +29,25 @@
  * scratch space (the row plan) from a stream-ordered pool per device, so
  * calls on different streams do not share scratch.  It keeps one scratch
  * block (and, for FusedMM's two-launch route and the element-balanced
- * kernel, one work buffer) per stream it has been called on, grown when a
- * call needs more, until the process ends.
+ * kernel, one work buffer) per (device, stream handle) it has been called
+ * on, grown when a call needs more, until spmm_stream_release is called on
+ * that stream or the process ends.  The blocks are keyed by the handle's
+ * value: a stream that is destroyed while the library still holds blocks
+ * for it leaves them to whatever stream later receives the same handle,
+ * possibly while the destroyed stream's last calls are still running.  Call
+ * spmm_stream_release(stream) before hipStreamDestroy(stream).
  *
  * Asynchrony: a call only enqueues work on `stream` (a hipStream_t; NULL is
  * the null stream) and returns; it never waits for the device.  Inputs must
  * stay alive, and C must not be read, until the stream has passed the call.
- * Calls may come from several host threads at once; calls on different
- * streams may run on the device at the same time (each stream has its own
- * scratch), and calls on one stream run one after another.
+ *
+ * Threads: calls may come from several host threads at once, on one stream
+ * or on several.  A call holds a per-(device, stream) lock from the moment
+ * it takes its share of the stream's scratch until its launches are
+ * enqueued, so calls on one stream reach the device one after another in
+ * the order they took the lock (the order of calls made from different
+ * threads at once is not otherwise defined).  Calls on different streams
+ * may run on the device at the same time: each stream has its own scratch.
  *
  * Errors: every call returns a status; nothing throws across the ABI.
  * Argument errors are found on the host before any HIP call.  The contents
@@ -176,14 +186,20 @@ spmm_status_t spmm_timing_read(double *plan_ms, double *worker_ms,
  * The same product C = A * B (either element type), computed by the
  * element-balanced kernel instead of the row plan: [Sgap] "Sgap: Towards
  * Efficient Sparse Tensor Algebra Compilation for GPU", the element-balanced
- * points of atomic parallelism and the grouped segmented reduction.  The
- * stored entries are split into equal spans, one per wavefront; partial sums
- * of entries that share a row are combined across lane groups in entry
- * order, and the rows cut by span ends go through carry slots that a second
- * launch adds up in order, so results repeat bit for bit (no atomics).
- * Arguments, layout, ownership and errors as for spmm_csr_tuned (dtype is
- * SPMM_DTYPE_F32 or SPMM_DTYPE_BF16); the carry slots (2 rows of N floats
- * per wavefront of the GPU) are kept per stream by the library.
+ * points of atomic parallelism and the grouped segmented reduction.  One
+ * launch.  The stored entries are split into equal spans, one per
+ * wavefront; partial sums of entries that share a row are combined across
+ * lane groups in entry order.  A row cut by a span end is finished inside
+ * the same launch: each wavefront that holds part of it writes its partial
+ * row to a carry slot and then arrives on the row's counter (a
+ * compare-and-swap on a word tagged with the call's epoch); the arrival that
+ * completes the count adds the row's slots in span order and stores the
+ * row.  No atomic adds touch C and the summation order is fixed, so results
+ * repeat bit for bit.  Arguments, layout, ownership and errors as for
+ * spmm_csr_tuned (dtype is SPMM_DTYPE_F32 or SPMM_DTYPE_BF16).  The carry
+ * slots (2 rows of N floats per wavefront of the GPU) live in the stream's
+ * work buffer, the arrival counters in the stream's plan scratch; the call
+ * takes one epoch of that scratch like a product call.
  */
 spmm_status_t spmm_csr_eb(int32_t dtype, const int32_t *rowptr,
                           const int32_t *colind, const void *vals,
@@ -269,15 +285,27 @@ spmm_status_t fusedmm_csr_bf16in_f32acc(const int32_t *rowptr,
                                         int64_t N, int64_t nnz, void *stream);
 
 /*
- * Health check for tests.  Inside a call, product wavefronts poll for the
- * plan entries they need while the plan workgroups of the same launch write
+ * Health check.  Inside a call, product wavefronts poll for the plan
+ * entries they need while the plan workgroups of the same launch write
  * them; each poll is bounded (about a second), and an item whose entry
  * never became visible is left undone and counted.  spmm_stream_faults
  * waits for `stream`, returns in *faults the number of such items since the
- * stream's scratch was created or last queried, and resets it.  The count
- * is 0 unless the plan workgroups were kept from running.
+ * stream's scratch was created or last queried, and resets it.  A non-zero
+ * count means that the outputs of the calls since the last query are not
+ * valid.  The count is 0 unless the plan workgroups were kept from running.
  */
 spmm_status_t spmm_stream_faults(void *stream, int64_t *faults);
+
+/*
+ * Give back the scratch block and the work buffer the library keeps for
+ * `stream` on the current device: both are freed in stream order after
+ * the calls already enqueued on it, and the stream is then synchronised,
+ * so the caller may destroy the stream afterwards.  A later call on the
+ * same handle allocates fresh blocks.  No other call on this stream may be
+ * in progress in another thread.  Success (and nothing done) if the
+ * library holds nothing for the stream.
+ */
+spmm_status_t spmm_stream_release(void *stream);
 
 #ifdef __cplusplus
 }

@@ -31,6 +31,7 @@ from ._binding import (  # noqa: F401
     spmm_csr_tuned,
     status_string,
     stream_faults,
+    stream_release,
     timing_enable,
     timing_read,
 )

@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
                                    ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_int64)]
     L.spmm_stream_faults.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]
+    L.spmm_stream_release.argtypes = [ctypes.c_void_p]
     L.sddmm_csr_f32.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
     L.sddmm_csr_bf16in_f32acc.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
     L.fusedmm_csr_f32.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
@@ -87,7 +88,7 @@ def lib() -> ctypes.CDLL:
         getattr(L, name).restype = I32
     for name in ("spmm_csr_f32", "spmm_csr_bf16in_f32acc", "spmm_csr_tuned",
                  "spmm_resolve_tuning", "spmm_plan_export", "spmm_timing_enable",
-                 "spmm_timing_read", "spmm_stream_faults"):
+                 "spmm_timing_read", "spmm_stream_faults", "spmm_stream_release"):
         getattr(L, name).restype = I32
     _lib = L
     return L
@@ -406,3 +407,11 @@ def stream_faults(stream=None) -> int:
     _check(lib().spmm_stream_faults(_stream_handle(None, stream), ctypes.byref(n)),
            "spmm_stream_faults")
     return n.value
+
+
+def stream_release(stream=None) -> None:
+    """Free the scratch the library keeps for `stream` (default: torch's
+    current stream) after the calls already enqueued on it, and wait for
+    the stream; call before the stream is destroyed."""
+    _check(lib().spmm_stream_release(_stream_handle(None, stream)),
+           "spmm_stream_release")

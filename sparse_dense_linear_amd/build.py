@@ -20,7 +20,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libsdl_spmm.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["api.hip", "plan.hip", "worker.hip", "sddmm.hip", "eb.hip"]
+SOURCES = ["api.hip", "plan.hip", "worker.hip", "sddmm.hip", "eb.hip",
+           "worker_f32_buf.hip", "worker_f32_flat.hip", "worker_bf16_buf.hip",
+           "worker_bf16_flat.hip", "worker_fused_buf.hip", "worker_fused_flat.hip"]
 CEILING_SOURCE = "ceiling.hip"
 CEILING_PATH = os.path.join(HERE, "libsdl_ceiling.so")
 ARCH = "gfx950"
@@ -58,7 +60,7 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")
         return obj
 
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES) + 1, os.cpu_count() or 4)) as ex:
         objs = list(ex.map(one, SOURCES + [CEILING_SOURCE]))
     for target, parts in ((LIB_PATH, objs[:-1]), (CEILING_PATH, objs[-1:])):
         tmp = target + ".tmp"

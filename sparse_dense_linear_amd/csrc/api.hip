@@ -11,6 +11,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -186,24 +188,45 @@ bool test_fail_alloc()
     return v != nullptr && v[0] == '1';
 }
 
-// Scratch space is kept per (device, stream) and reused by later calls on
-// the same stream, which stream order serialises.  A block that is too
-// small is replaced (allocate and zero the larger one, free the old one,
-// all stream-ordered).  Calls on different streams never share scratch.
-// Each call on a block gets the next epoch; epoch 0 never occurs, so the
-// zeroed block holds no valid word.
-struct StreamScratch {
-    int dev;
-    hipStream_t stream;
-    void *ptr;
-    size_t size;
-    uint32_t epoch;   // last epoch used on this block
+// Per-(device, stream) state: the plan scratch block, the work buffer and
+// the last epoch.  A call holds the state's mutex from the moment it picks
+// its epoch and buffers until all of its launches are enqueued, so calls
+// made on one stream from several host threads reach the stream in epoch
+// order, and a buffer replaced by a growing call is freed (stream-ordered)
+// only after every launch that uses it has been enqueued.  Calls on
+// different streams never share scratch.  Each call on a block gets the next
+// epoch; epoch 0 never occurs, so a zeroed block holds no valid word.
+// States are never deleted (spmm_stream_release empties one), so a pointer
+// to one stays valid for the life of the process.
+struct StreamState {
+    int dev = 0;
+    hipStream_t stream = nullptr;
+    std::mutex mu;
+    void *scratch = nullptr;    // plan scratch block (zeroed when created)
+    size_t scratch_size = 0;
+    uint32_t epoch = 0;         // last epoch used on the block
+    void *aux = nullptr;        // work buffer (FusedMM values, carry slots)
+    size_t aux_size = 0;
 };
 
-std::mutex g_scratch_mu;
-std::vector<StreamScratch> g_scratch;
+std::mutex g_registry_mu;
+std::vector<std::unique_ptr<StreamState>> g_streams;
 
-hipError_t fresh_block(int dev, hipStream_t stream, size_t size, void **out)
+StreamState *stream_state(int dev, hipStream_t stream, bool create)
+{
+    std::lock_guard<std::mutex> lock(g_registry_mu);
+    for (auto &e : g_streams)
+        if (e->dev == dev && e->stream == stream)
+            return e.get();
+    if (!create)
+        return nullptr;
+    g_streams.emplace_back(new StreamState);
+    g_streams.back()->dev = dev;
+    g_streams.back()->stream = stream;
+    return g_streams.back().get();
+}
+
+hipError_t fresh_block(int dev, hipStream_t stream, size_t size, bool zero, void **out)
 {
     hipMemPool_t pool;
     hipError_t err = pool_for_device(dev, &pool);
@@ -215,8 +238,7 @@ hipError_t fresh_block(int dev, hipStream_t stream, size_t size, void **out)
         return err;
     if (ptr == nullptr)
         return hipErrorOutOfMemory;
-    err = hipMemsetAsync(ptr, 0, size, stream);
-    if (err != hipSuccess) {
+    if (zero && (err = hipMemsetAsync(ptr, 0, size, stream)) != hipSuccess) {
         hipFreeAsync(ptr, stream);
         return err;
     }
@@ -224,85 +246,56 @@ hipError_t fresh_block(int dev, hipStream_t stream, size_t size, void **out)
     return hipSuccess;
 }
 
-// Scratch block of at least `need` bytes for this stream, and the epoch the
-// caller's launch must use.
-hipError_t scratch_for(int dev, hipStream_t stream, size_t need, void **out,
-                       uint32_t *epoch)
+// Scratch block of at least `need` bytes for the stream of `ss` (whose
+// mutex the caller holds), and the epoch the caller's launch must use.  A
+// block that is too small (or whose epochs are used up) is replaced: the
+// larger one is allocated and zeroed, the old one freed, all in stream
+// order after the launches already enqueued on the stream.
+hipError_t scratch_for(StreamState &ss, size_t need, void **out, uint32_t *epoch)
 {
-    std::lock_guard<std::mutex> lock(g_scratch_mu);
-    StreamScratch *slot = nullptr;
-    for (StreamScratch &e : g_scratch)
-        if (e.dev == dev && e.stream == stream)
-            slot = &e;
-    if (slot && slot->size >= need && slot->epoch != UINT32_MAX) {
-        *out = slot->ptr;
-        *epoch = ++slot->epoch;
+    if (ss.scratch && ss.scratch_size >= need && ss.epoch != UINT32_MAX) {
+        *out = ss.scratch;
+        *epoch = ++ss.epoch;
         return hipSuccess;
     }
     size_t size = need;
-    if (slot && size < slot->size + slot->size / 4)
-        size = slot->size + slot->size / 4;
+    if (ss.scratch && size < ss.scratch_size + ss.scratch_size / 4)
+        size = ss.scratch_size + ss.scratch_size / 4;
     void *ptr = nullptr;
-    hipError_t err = fresh_block(dev, stream, size, &ptr);
+    hipError_t err = fresh_block(ss.dev, ss.stream, size, true, &ptr);
     if (err != hipSuccess)
         return err;
-    if (slot) {
-        hipFreeAsync(slot->ptr, stream);
-        slot->ptr = ptr;
-        slot->size = size;
-        slot->epoch = 1;
-    } else {
-        g_scratch.push_back(StreamScratch{dev, stream, ptr, size, 1});
-    }
+    if (ss.scratch)
+        hipFreeAsync(ss.scratch, ss.stream);
+    ss.scratch = ptr;
+    ss.scratch_size = size;
+    ss.epoch = 1;
     *out = ptr;
     *epoch = 1;
     return hipSuccess;
 }
 
-// A second per-stream buffer for work arrays whose contents do not outlive
-// a call (FusedMM's values, the element-balanced kernel's carry slots).  It
-// only grows; calls on one stream are ordered, so reusing it is safe.  Not
-// cleared (every call writes what it reads).
-struct StreamAux {
-    int dev;
-    hipStream_t stream;
-    void *ptr;
-    size_t size;
-};
-
-std::vector<StreamAux> g_aux;
-
-hipError_t aux_for(int dev, hipStream_t stream, size_t need, void **out)
+// The stream's work buffer, for arrays whose contents do not outlive a call
+// (FusedMM's values, the element-balanced kernel's carry slots).  It only
+// grows; the caller holds the state's mutex.  Not cleared (every call writes
+// what it reads).
+hipError_t aux_for(StreamState &ss, size_t need, void **out)
 {
-    std::lock_guard<std::mutex> lock(g_scratch_mu);
-    StreamAux *slot = nullptr;
-    for (StreamAux &e : g_aux)
-        if (e.dev == dev && e.stream == stream)
-            slot = &e;
-    if (slot && slot->size >= need) {
-        *out = slot->ptr;
+    if (ss.aux && ss.aux_size >= need) {
+        *out = ss.aux;
         return hipSuccess;
     }
-    hipMemPool_t pool;
-    hipError_t err = pool_for_device(dev, &pool);
-    if (err != hipSuccess)
-        return err;
     size_t size = need;
-    if (slot && size < slot->size + slot->size / 4)
-        size = slot->size + slot->size / 4;
+    if (ss.aux && size < ss.aux_size + ss.aux_size / 4)
+        size = ss.aux_size + ss.aux_size / 4;
     void *ptr = nullptr;
-    err = hipMallocFromPoolAsync(&ptr, size, pool, stream);
+    hipError_t err = fresh_block(ss.dev, ss.stream, size, false, &ptr);
     if (err != hipSuccess)
         return err;
-    if (ptr == nullptr)
-        return hipErrorOutOfMemory;
-    if (slot) {
-        hipFreeAsync(slot->ptr, stream);
-        slot->ptr = ptr;
-        slot->size = size;
-    } else {
-        g_aux.push_back(StreamAux{dev, stream, ptr, size});
-    }
+    if (ss.aux)
+        hipFreeAsync(ss.aux, ss.stream);
+    ss.aux = ptr;
+    ss.aux_size = size;
     *out = ptr;
     return hipSuccess;
 }
@@ -371,7 +364,8 @@ spmm_status_t run_with(int32_t dtype, const int32_t *rowptr,
                        bool own_events, hipEvent_t e0, hipEvent_t e1,
                        bool vals_relative = false,
                        const void *dot_rows = nullptr,
-                       const void *dot_cols = nullptr)
+                       const void *dot_cols = nullptr,
+                       StreamState *held = nullptr)
 {
     spmm_status_t st = check_args(dtype, rowptr, B, C, M, K, N);
     if (st != SPMM_SUCCESS)
@@ -386,14 +380,22 @@ spmm_status_t run_with(int32_t dtype, const int32_t *rowptr,
         return fail(SPMM_ERROR_OUT_OF_MEMORY, "allocation failure forced by SPMM_TEST_FAIL_ALLOC");
 
     hipStream_t stream = (hipStream_t)stream_ptr;
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err != hipSuccess)
-        return fail_hip(err, "hipGetDevice");
+    hipError_t err = hipSuccess;
+    // `held`: the caller (FusedMM's two-launch route) holds the stream's
+    // mutex already; otherwise take it here, until the launch is enqueued.
+    std::unique_lock<std::mutex> guard;
+    StreamState *ss = held;
+    if (ss == nullptr) {
+        int dev = 0;
+        if ((err = hipGetDevice(&dev)) != hipSuccess)
+            return fail_hip(err, "hipGetDevice");
+        ss = stream_state(dev, stream, true);
+        guard = std::unique_lock<std::mutex>(ss->mu);
+    }
     const ScratchLayout lay = scratch_layout(M);
     void *scratch = nullptr;
     uint32_t epoch = 0;
-    err = scratch_for(dev, stream, (size_t)lay.total, &scratch, &epoch);
+    err = scratch_for(*ss, (size_t)lay.total, &scratch, &epoch);
     if (err == hipErrorOutOfMemory)
         return fail(SPMM_ERROR_OUT_OF_MEMORY, "scratch allocation failed");
     if (err != hipSuccess)
@@ -558,7 +560,9 @@ spmm_status_t run_fusedmm(const int32_t *rowptr, const int32_t *colind,
         ((uintptr_t)B) % 16 == 0)
         return run_with(SPMM_DTYPE_F32, rowptr, colind, nullptr, D, E, M, K, N,
                         nullptr, stream_ptr, false, nullptr, nullptr, false, C, B);
-    // Otherwise two launches: SDDMM into a value array, then the product.
+    // Otherwise two launches: SDDMM into a value array, then the product,
+    // both enqueued under the stream's mutex (the value array is the
+    // stream's work buffer).
     hipStream_t stream = (hipStream_t)stream_ptr;
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
@@ -568,7 +572,9 @@ spmm_status_t run_fusedmm(const int32_t *rowptr, const int32_t *colind,
     const size_t bytes = (size_t)(nnz > 0 ? nnz : 1) * sizeof(float);
     if (test_fail_alloc())
         return fail(SPMM_ERROR_OUT_OF_MEMORY, "allocation failure forced by SPMM_TEST_FAIL_ALLOC");
-    err = aux_for(dev, stream, bytes, (void **)&vals);
+    StreamState *ss = stream_state(dev, stream, true);
+    std::lock_guard<std::mutex> guard(ss->mu);
+    err = aux_for(*ss, bytes, (void **)&vals);
     if (err == hipErrorOutOfMemory)
         return fail(SPMM_ERROR_OUT_OF_MEMORY, "value scratch allocation failed");
     if (err != hipSuccess)
@@ -603,7 +609,7 @@ spmm_status_t run_fusedmm(const int32_t *rowptr, const int32_t *colind,
     if (st == SPMM_SUCCESS)
         st = run_with(SPMM_DTYPE_F32, rowptr, colind, vals, D, E, M, K, N, nullptr,
                       stream_ptr, true, nnz > 0 ? nullptr : tc.work0, tc.work1,
-                      true);
+                      true, nullptr, nullptr, ss);
     if (st == SPMM_SUCCESS && timing) {
         std::lock_guard<std::mutex> lock(g_time_mu);
         g_timed.push_back(tc);
@@ -671,14 +677,16 @@ spmm_status_t run_eb(int32_t dtype, const int32_t *rowptr, const int32_t *colind
     const ScratchLayout lay = scratch_layout(M > waves ? M : waves);
     void *scratch = nullptr;
     uint32_t epoch = 0;
-    err = scratch_for(dev, stream, (size_t)lay.total, &scratch, &epoch);
+    StreamState *ss = stream_state(dev, stream, true);
+    std::lock_guard<std::mutex> guard(ss->mu);  // until the launch is enqueued
+    err = scratch_for(*ss, (size_t)lay.total, &scratch, &epoch);
     if (err == hipErrorOutOfMemory)
         return fail(SPMM_ERROR_OUT_OF_MEMORY, "scratch allocation failed");
     if (err != hipSuccess)
         return fail_hip(err, "scratch allocation");
     const size_t bytes = (size_t)(2 * waves) * (size_t)N * sizeof(float);
     char *mem = nullptr;
-    err = aux_for(dev, stream, bytes, (void **)&mem);
+    err = aux_for(*ss, bytes, (void **)&mem);
     if (err == hipErrorOutOfMemory)
         return fail(SPMM_ERROR_OUT_OF_MEMORY, "carry allocation failed");
     if (err != hipSuccess)
@@ -948,6 +956,34 @@ spmm_status_t spmm_timing_read(double *plan_ms, double *worker_ms,
     return st;
 }
 
+spmm_status_t spmm_stream_release(void *stream_ptr)
+{
+    g_last_error.clear();
+    hipStream_t stream = (hipStream_t)stream_ptr;
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return fail_hip(err, "hipGetDevice");
+    StreamState *ss = stream_state(dev, stream, false);
+    if (ss == nullptr)
+        return SPMM_SUCCESS;  // never called on this stream
+    std::lock_guard<std::mutex> guard(ss->mu);
+    // stream-ordered frees after the calls already enqueued, then wait, so
+    // that the stream can be destroyed and its handle reused safely
+    if (ss->scratch && (err = hipFreeAsync(ss->scratch, stream)) != hipSuccess)
+        return fail_hip(err, "hipFreeAsync");
+    ss->scratch = nullptr;
+    ss->scratch_size = 0;
+    ss->epoch = 0;
+    if (ss->aux && (err = hipFreeAsync(ss->aux, stream)) != hipSuccess)
+        return fail_hip(err, "hipFreeAsync");
+    ss->aux = nullptr;
+    ss->aux_size = 0;
+    if ((err = hipStreamSynchronize(stream)) != hipSuccess)
+        return fail_hip(err, "hipStreamSynchronize");
+    return SPMM_SUCCESS;
+}
+
 spmm_status_t spmm_stream_faults(void *stream_ptr, int64_t *faults)
 {
     g_last_error.clear();
@@ -959,15 +995,13 @@ spmm_status_t spmm_stream_faults(void *stream_ptr, int64_t *faults)
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess)
         return fail_hip(err, "hipGetDevice");
-    void *block = nullptr;
-    {
-        std::lock_guard<std::mutex> lock(g_scratch_mu);
-        for (StreamScratch &e : g_scratch)
-            if (e.dev == dev && e.stream == stream)
-                block = e.ptr;
-    }
-    if (block == nullptr)
+    StreamState *ss = stream_state(dev, stream, false);
+    if (ss == nullptr)
         return SPMM_SUCCESS;  // no call on this stream yet
+    std::lock_guard<std::mutex> guard(ss->mu);
+    void *block = ss->scratch;
+    if (block == nullptr)
+        return SPMM_SUCCESS;  // no block (yet, or released)
     uint32_t *word = (uint32_t *)((char *)block + scratch_layout(0).faults);
     uint32_t v = 0;
     if ((err = hipMemcpyAsync(&v, word, sizeof v, hipMemcpyDeviceToHost, stream)) != hipSuccess ||

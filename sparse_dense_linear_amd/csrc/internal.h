@@ -120,6 +120,20 @@ struct WorkerArgs {
 hipError_t launch_worker(const WorkerConfig &cfg, const WorkerArgs &args,
                          hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
+// The launchers of the product kernel's variants, one per source file
+// (worker_<kind>_<buf|flat>.hip): fp32, bf16 and FusedMM forms, with B
+// behind a buffer resource (below 4 GiB) or flat 64-bit addresses.
+#define SDL_DECLARE_LAUNCH(name)                                                \
+    hipError_t name(const WorkerConfig &cfg, const WorkerArgs &a, hipStream_t s, \
+                    hipEvent_t e0, hipEvent_t e1);
+SDL_DECLARE_LAUNCH(launch_f32_buf)
+SDL_DECLARE_LAUNCH(launch_f32_flat)
+SDL_DECLARE_LAUNCH(launch_bf16_buf)
+SDL_DECLARE_LAUNCH(launch_bf16_flat)
+SDL_DECLARE_LAUNCH(launch_fused_buf)
+SDL_DECLARE_LAUNCH(launch_fused_flat)
+#undef SDL_DECLARE_LAUNCH
+
 // One SDDMM call (sddmm.hip): A[p - rowptr[0]] = <C_i, B_colind[p]>.
 struct SddmmArgs {
     int dtype;               // SPMM_DTYPE_*: both dense operands

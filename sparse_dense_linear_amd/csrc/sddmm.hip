@@ -29,6 +29,8 @@
 //     and a reduce-scatter leaves entry u's total in one lane (63 shuffles
 //     per lane instead of 6 per entry), summed in the butterfly's order.
 #include <hip/hip_ext.h>
+
+#include <atomic>
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -248,7 +250,10 @@ template <class S>
 hipError_t launch_sd(const SddmmArgs &a, hipStream_t stream, hipEvent_t e0,
                      hipEvent_t e1)
 {
-    static int resident_blocks = 0;
+    // Workgroups of this variant that fit on the GPU at once; queried once
+    // (several host threads may race to store the same value).
+    static std::atomic<int> resident_cache{0};
+    int resident_blocks = resident_cache.load(std::memory_order_relaxed);
     if (resident_blocks == 0) {
         int dev = 0, per_cu = 0, cus = 0;
         hipError_t err = hipGetDevice(&dev);
@@ -260,6 +265,7 @@ hipError_t launch_sd(const SddmmArgs &a, hipStream_t stream, hipEvent_t e0,
         if (err != hipSuccess)
             return err;
         resident_blocks = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+        resident_cache.store(resident_blocks, std::memory_order_relaxed);
     }
     // Equal spans of whole 64-entry batches, one per resident wavefront
     // (fewer when there are fewer batches).

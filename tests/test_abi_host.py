@@ -29,7 +29,7 @@ def test_header_declares_entry_points():
     for must in ("spmm_csr_f32", "spmm_csr_bf16in_f32acc", "spmm_csr_tuned",
                  "spmm_resolve_tuning", "spmm_plan_export", "spmm_status_string",
                  "spmm_last_error", "spmm_timing_enable", "spmm_timing_read",
-                 "spmm_stream_faults", "sddmm_csr_f32", "sddmm_csr_bf16in_f32acc",
+                 "spmm_stream_faults", "spmm_stream_release", "sddmm_csr_f32", "sddmm_csr_bf16in_f32acc",
                  "fusedmm_csr_f32", "fusedmm_csr_bf16in_f32acc"):
         assert must in names
 

@@ -187,3 +187,77 @@ def test_host_threads_on_their_own_streams():
         Cref, Sref = oracle.spmm_ref(p.rowptr, p.colind, p.vals, p.B, p.N)
         assert_parity(C.reshape(p.M, p.N), Cref, Sref, "f32", f"thread {t}")
         assert_parity(E.reshape(p.M, p.N), Cref, Sref, "f32", f"thread {t} eb")
+
+
+def test_host_threads_on_one_stream():
+    """Four host threads share ONE stream.  Each issues products of growing
+    M (so the stream's scratch block is replaced by larger ones while other
+    threads' calls that use the old block are already enqueued), each
+    followed by an element-balanced call (which takes an epoch and clears
+    the next queue set).  The library holds the stream's lock from a call's
+    choice of epoch and block until its launch is enqueued, so epochs reach
+    the stream in order; every result is checked against the oracle."""
+    import threading
+
+    sizes = [(3000, 15000, 60000), (5000, 25000, 45000),
+             (2000, 35000, 70000), (8000, 12000, 80000)]
+    problems = [[W.powerlaw_rows(M=m, N=64, seed=70 + 10 * t + k)
+                 for k, m in enumerate(sizes[t])] for t in range(4)]
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs, errors = {}, []
+    start = threading.Barrier(4)
+
+    def work(t):
+        try:
+            with torch.cuda.stream(s):
+                bufs = []
+                for p in problems[t]:
+                    a = _dev(p)
+                    C = torch.full((p.M * p.N,), float("nan"), device="cuda")
+                    E = torch.full((p.M * p.N,), float("nan"), device="cuda")
+                    bufs.append((p, a, C, E))
+                s.synchronize()
+                start.wait(timeout=60)
+                for _ in range(3):
+                    for p, a, C, E in bufs:
+                        sdl.spmm_csr_f32(*a, C, p.M, p.K, p.N, stream=s)
+                        sdl.spmm_csr_eb(sdl.DTYPE_F32, *a, E, p.M, p.K, p.N, stream=s)
+            outs[t] = bufs
+        except Exception as exc:           # reported by the main thread
+            errors.append(exc)
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not errors, errors
+    s.synchronize()
+    assert sdl.stream_faults(s) == 0
+    for t in range(4):
+        for p, _, C, E in outs[t]:
+            Cref, Sref = oracle.spmm_ref(p.rowptr, p.colind, p.vals, p.B, p.N)
+            assert_parity(C.cpu().numpy().reshape(p.M, p.N), Cref, Sref, "f32",
+                          f"thread {t} M={p.M}")
+            assert_parity(E.cpu().numpy().reshape(p.M, p.N), Cref, Sref, "f32",
+                          f"thread {t} M={p.M} eb")
+    sdl.stream_release(s)
+
+
+def test_stream_release_then_reuse():
+    """After spmm_stream_release the stream's blocks are gone; the next call
+    on the same stream allocates fresh ones and is still correct."""
+    p = W.powerlaw_rows(M=30000, N=64, seed=91)
+    a = _dev(p)
+    s = torch.cuda.Stream()
+    C = torch.full((p.M * p.N,), float("nan"), device="cuda")
+    Cref, Sref = oracle.spmm_ref(p.rowptr, p.colind, p.vals, p.B, p.N)
+    for _ in range(2):
+        with torch.cuda.stream(s):
+            sdl.spmm_csr_f32(*a, C, p.M, p.K, p.N, stream=s)
+            sdl.spmm_csr_eb(sdl.DTYPE_F32, *a, C, p.M, p.K, p.N, stream=s)
+        sdl.stream_release(s)        # waits for the stream
+        assert_parity(C.cpu().numpy().reshape(p.M, p.N), Cref, Sref, "f32", "release")
+        C.fill_(float("nan"))
+    sdl.stream_release(s)            # nothing held: a no-op
