@@ -9,6 +9,8 @@ Pages cited:
   [IntelMax] "Performance Optimization of Deep Learning Sparse Matrix Kernels
              on Intel Max Series GPU"
   [Sgap]     "Sgap: Towards Efficient Sparse Tensor Algebra Compilation for GPU"
+  [Multilevel] "Sparse Matrix-Matrix Multiplication on Multilevel Memory
+             Architectures: Algorithms and Experiments"
 
 Contents
   spmm_ref   -- C = A*B and the bound S = |A|*|B| in fp64 ([IntelMax], SpMM
@@ -19,8 +21,9 @@ Contents
   fusedmm_ref -- E_i = sum_p <C_i, B_j> D_j over the pattern and its bound
                 ([IntelMax], FusedMM operation, Fig. 6 / Algorithm 3),
                 computed by ``sddmm_ref.c``.
-  plan_ref   -- the row-binning plan: which rows are short, medium or long, and
-                how long rows are cut into nnz chunks (see its docstring).
+  plan_ref   -- the row-binning plan: which rows are short, medium, long or
+                hub rows, how long rows are cut into nnz chunks and hub rows
+                into column-slab chunks (see its docstring).
   widen_bf16 -- exact bf16 -> float64 widening used by the oracle.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against values
@@ -275,7 +278,9 @@ def widen_bf16(bits) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
-def plan_ref(rowptr, short_max: int, medium_max: int, chunk_nnz: int) -> dict:
+def plan_ref(rowptr, short_max: int, medium_max: int, chunk_nnz: int,
+             hub_min: int | None = None, slab_rows: int | None = None,
+             K: int | None = None, colind=None) -> dict:
     """Row-binning plan, derived plainly on the CPU.
 
     The pages motivate two ways to hand out the work of a row: one worker per
@@ -288,25 +293,49 @@ def plan_ref(rowptr, short_max: int, medium_max: int, chunk_nnz: int) -> dict:
       len_i = rowptr[i+1] - rowptr[i]
       short  : len_i <= short_max
       medium : short_max < len_i <= medium_max
-      long   : len_i > medium_max, cut into n_i = ceil(len_i / chunk_nnz)
+      long   : medium_max < len_i <= H, cut into n_i = ceil(len_i / chunk_nnz)
                chunks; chunk k (0 <= k < n_i) covers positions
                [rowptr[i] + floor(k*len_i/n_i), rowptr[i] + floor((k+1)*len_i/n_i)),
                so the chunks tile the row in order and none exceeds chunk_nnz.
+      hub    : len_i > H, where H = max(hub_min, medium_max) (no hub rows when
+               hub_min is None).  A hub row is cut by columns instead: with
+               n_slabs = ceil(K / slab_rows), hub chunk s (0 <= s < n_slabs)
+               covers positions [b(s), b(s+1)), where b(s) is rowptr[i] plus
+               the number of the row's entries whose column is below
+               s * slab_rows, b(0) = rowptr[i] and b(n_slabs) = rowptr[i+1].
+               For a row whose columns ascend, chunk s holds exactly its
+               entries with columns in [s*slab_rows, (s+1)*slab_rows) -- the
+               rows of B that one column slab holds ([Multilevel], the access
+               pattern: row j of B is read once per non-zero in column j, so
+               entries of many rows that fall in one slab reuse the same rows
+               of B).  The bounds are stated for ascending rows only.
 
-    Lists are in ascending row order; chunks are ordered by row, then by k.
+    Lists are in ascending row order; chunks are ordered by row, then by k;
+    hub chunks slab-major: all hubs' chunks of slab 0 (in hub order), then
+    slab 1, and so on.
     Returns a dict of int32 arrays:
       medium_rows [n_medium]
       long_rows   [n_long, 3]   (row, first chunk index, number of chunks)
       chunks      [n_chunks, 4] (row, p0, p1, index of the row in long_rows)
-    plus the integer counts n_short, n_medium, n_long, n_chunks.
+      hub_rows    [n_hub]
+      hub_chunks  [n_hub * n_slabs, 4] (row, p0, p1, index of the row in hub_rows)
+    plus the integer counts n_short, n_medium, n_long, n_chunks, n_hub,
+    n_slabs (0 without hub rows).
     """
     if not (0 <= short_max <= medium_max) or chunk_nnz < 1:
         raise ValueError("need 0 <= short_max <= medium_max and chunk_nnz >= 1")
     rp = np.asarray(rowptr, dtype=np.int64)
     lengths = rp[1:] - rp[:-1]
+    if hub_min is None:
+        top = np.iinfo(np.int64).max
+    else:
+        if slab_rows is None or slab_rows < 1 or K is None or K < 1 or colind is None:
+            raise ValueError("hub rows need slab_rows >= 1, K >= 1 and colind")
+        top = max(int(hub_min), int(medium_max))
     is_short = lengths <= short_max
     is_medium = (lengths > short_max) & (lengths <= medium_max)
-    is_long = lengths > medium_max
+    is_long = (lengths > medium_max) & (lengths <= top)
+    is_hub = lengths > top
     medium_rows = np.nonzero(is_medium)[0].astype(np.int32)
     long_ids = np.nonzero(is_long)[0]
     long_rows = []
@@ -320,12 +349,33 @@ def plan_ref(rowptr, short_max: int, medium_max: int, chunk_nnz: int) -> dict:
             p0 = start + (k * length) // n
             p1 = start + ((k + 1) * length) // n
             chunks.append((int(row), p0, p1, li))
+    hub_ids = np.nonzero(is_hub)[0]
+    n_slabs = -(-int(K) // int(slab_rows)) if hub_min is not None else 0
+    hub_chunks = []
+    if hub_ids.size:
+        cols = np.asarray(colind, dtype=np.int64)
+        bounds = []                      # per hub: b(0) .. b(n_slabs)
+        for row in hub_ids:
+            start, end = int(rp[row]), int(rp[row + 1])
+            row_cols = cols[start:end]
+            b = [start]
+            for s in range(1, n_slabs):
+                b.append(start + int(np.count_nonzero(row_cols < s * slab_rows)))
+            b.append(end)
+            bounds.append(b)
+        for s in range(n_slabs):
+            for hi, row in enumerate(hub_ids):
+                hub_chunks.append((int(row), bounds[hi][s], bounds[hi][s + 1], hi))
     return {
         "n_short": int(is_short.sum()),
         "n_medium": int(medium_rows.shape[0]),
         "n_long": len(long_rows),
         "n_chunks": len(chunks),
+        "n_hub": int(hub_ids.shape[0]),
+        "n_slabs": n_slabs,
         "medium_rows": medium_rows,
         "long_rows": np.array(long_rows, dtype=np.int32).reshape(-1, 3),
         "chunks": np.array(chunks, dtype=np.int32).reshape(-1, 4),
+        "hub_rows": hub_ids.astype(np.int32),
+        "hub_chunks": np.array(hub_chunks, dtype=np.int32).reshape(-1, 4),
     }
