@@ -135,6 +135,34 @@ spmm_status_t spmm_csr_tuned(int32_t dtype, const int32_t *rowptr,
                              void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * product of spmm_csr_tuned -- same arguments, checks, thresholds, kernel
+ * and results -- with its plan scratch in a fixed array that the library
+ * holds on each GPU it runs on, instead of a per-stream block from a pool.
+ * This entry point calls no hipMalloc, hipFree or other allocating routine
+ * (and allocates nothing on the host).
+ *
+ * Limit: the fixed array holds 12 MiB, enough for the plan of M up to
+ * 311,000 rows (about 40 bytes per row); a larger M returns
+ * SPMM_ERROR_UNSUPPORTED, found on the host before any HIP call, with the
+ * exact limit in spmm_last_error().
+ *
+ * Every call of this entry point on one GPU uses that GPU's single array,
+ * which keeps the last call's contents (plan words tagged with a per-GPU
+ * call counter, so nothing needs clearing).  Calls are enqueued one at a
+ * time (a per-GPU lock), but calls that overlap on the device -- e.g. made
+ * on two streams of one GPU without ordering between them -- race on the
+ * array and give wrong results: order them on one stream or with events.
+ * The fault count of these calls is not reported by spmm_stream_faults.
+ */
+spmm_status_t spmm_csr_tuned_noalloc(int32_t dtype, const int32_t *rowptr,
+                                     const int32_t *colind, const void *vals,
+                                     const void *B, float *C, int64_t M,
+                                     int64_t K, int64_t N,
+                                     const spmm_tuning_t *tuning, void *stream);
+
+/*
  * Host only, no HIP call: the thresholds a call with this dtype, N and
  * requested tuning (NULL = all defaults) would use, written to *resolved.
  */

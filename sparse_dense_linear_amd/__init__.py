@@ -29,6 +29,7 @@ from ._binding import (  # noqa: F401
     spmm_csr_eb,
     spmm_csr_f32,
     spmm_csr_tuned,
+    spmm_csr_tuned_noalloc,
     status_string,
     stream_faults,
     stream_release,

@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.spmm_csr_bf16in_f32acc.argtypes = [P, P, P, P, P, I64, I64, I64, P]
     L.spmm_csr_tuned.argtypes = [I32, P, P, P, P, P, I64, I64, I64,
                                  ctypes.POINTER(_TuningStruct), P]
+    L.spmm_csr_tuned_noalloc.argtypes = [I32, P, P, P, P, P, I64, I64, I64,
+                                         ctypes.POINTER(_TuningStruct), P]
     L.spmm_resolve_tuning.argtypes = [I32, I64, ctypes.POINTER(_TuningStruct),
                                       ctypes.POINTER(_TuningStruct)]
     L.spmm_plan_export.argtypes = [P, I64, ctypes.POINTER(_TuningStruct), P, I64,
@@ -87,6 +89,7 @@ def lib() -> ctypes.CDLL:
                  "fusedmm_csr_bf16in_f32acc", "spmm_csr_eb"):
         getattr(L, name).restype = I32
     for name in ("spmm_csr_f32", "spmm_csr_bf16in_f32acc", "spmm_csr_tuned",
+                 "spmm_csr_tuned_noalloc",
                  "spmm_resolve_tuning", "spmm_plan_export", "spmm_timing_enable",
                  "spmm_timing_read", "spmm_stream_faults", "spmm_stream_release"):
         getattr(L, name).restype = I32
@@ -188,6 +191,23 @@ def spmm_csr_tuned(dtype: int, rowptr, colind, vals, B, C, M: int, K: int,
                                 _ptr(B), _ptr(C), M, K, N, ts,
                                 _stream_handle(dev, stream)),
            "spmm_csr_tuned")
+
+
+def spmm_csr_tuned_noalloc(dtype: int, rowptr, colind, vals, B, C, M: int, K: int,
+                           N: int, tuning: Tuning | None = None, stream=None) -> None:
+    """spmm_csr_tuned with its plan scratch in the library's fixed per-GPU
+    array (spmm_csr_tuned_noalloc): no device allocation."""
+    torch = _torch()
+    if dtype == DTYPE_F32:
+        vd = bd = (torch.float32,)
+    else:
+        vd = bd = (torch.bfloat16, torch.int16, torch.uint16)
+    dev = _check_operands(rowptr, colind, vals, B, C, M, K, N, vd, bd)
+    ts = None if tuning is None else ctypes.byref(tuning._struct())
+    _check(lib().spmm_csr_tuned_noalloc(dtype, _ptr(rowptr), _ptr(colind), _ptr(vals),
+                                        _ptr(B), _ptr(C), M, K, N, ts,
+                                        _stream_handle(dev, stream)),
+           "spmm_csr_tuned_noalloc")
 
 
 def spmm_csr_eb(dtype: int, rowptr, colind, vals, B, C, M: int, K: int,

@@ -300,6 +300,77 @@ hipError_t aux_for(StreamState &ss, size_t need, void **out)
     return hipSuccess;
 }
 
+// ------------------------------------------------- fixed scratch (no allocation)
+
+// spmm_csr_tuned_noalloc takes its plan scratch from this fixed array
+// instead of the per-stream pool, so that it never allocates.  Every GPU the
+// library runs on holds its own copy (the array is part of the library's
+// device code object) until the process ends; every no-allocation call on a
+// GPU shares that GPU's copy.  The array is zero when the code object is
+// loaded, and plan words are tagged with a per-device epoch, so nothing is
+// cleared between calls; the queue counters of the next epoch are cleared by
+// each call itself (as for the per-stream blocks).
+constexpr size_t kFixedScratchBytes = (size_t)12 << 20;
+static __device__ __align__(256) char scratch[kFixedScratchBytes];
+
+// Host-side state of one device's copy: its device address (from
+// hipGetSymbolAddress with that device current -- the array's name is not
+// a device address in host code) and the last epoch used on it.  A fixed
+// table, so the no-allocation path allocates nothing on the host either.
+constexpr int kMaxDevices = 64;
+
+struct FixedScratch {
+    std::mutex mu;             // held from epoch choice to enqueue
+    char *ptr = nullptr;       // device address of `scratch` on this device
+    uint32_t epoch = 0;
+};
+
+FixedScratch g_fixed[kMaxDevices];
+
+// Fill kernel that zeroes the array when the per-device epochs run out (a
+// kernel rather than a memset, so that the call stays capturable).
+__global__ void zero_fixed_scratch(uint64_t *p, int64_t words)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+// The current device's copy of the array, its address looked up on first
+// use (with that device current).  Caller holds nothing.
+hipError_t fixed_scratch_for(int dev, FixedScratch **out)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    FixedScratch &fs = g_fixed[dev];
+    std::lock_guard<std::mutex> lock(fs.mu);
+    if (fs.ptr == nullptr) {
+        void *p = nullptr;
+        hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess)
+            return err;
+        if (p == nullptr)
+            return hipErrorInvalidSymbol;
+        fs.ptr = (char *)p;
+    }
+    *out = &fs;
+    return hipSuccess;
+}
+
+// Largest M whose plan scratch fits the fixed array.
+int64_t fixed_scratch_max_rows()
+{
+    int64_t lo = 0, hi = kMaxIndex - 1;
+    while (lo < hi) {
+        const int64_t mid = lo + (hi - lo + 1) / 2;
+        if ((size_t)scratch_layout(mid).total <= kFixedScratchBytes)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
 // --------------------------------------------------------------- timing
 
 // Kernel timing: the start/stop events are attached to the kernel dispatch
@@ -452,6 +523,73 @@ spmm_status_t run(int32_t dtype, const int32_t *rowptr, const int32_t *colind,
     g_last_error.clear();
     return run_with(dtype, rowptr, colind, vals, B, C, M, K, N, tuning,
                     stream_ptr, false, nullptr, nullptr);
+}
+
+// The product with the plan in the fixed scratch array: the same checks,
+// thresholds and kernel as spmm_csr_tuned; no allocation of any kind.
+spmm_status_t run_noalloc(int32_t dtype, const int32_t *rowptr,
+                          const int32_t *colind, const void *vals, const void *B,
+                          float *C, int64_t M, int64_t K, int64_t N,
+                          const spmm_tuning_t *tuning, void *stream_ptr)
+{
+    g_last_error.clear();
+    spmm_status_t st = check_args(dtype, rowptr, B, C, M, K, N);
+    if (st != SPMM_SUCCESS)
+        return st;
+    spmm_tuning_t t;
+    st = resolve(dtype, N, tuning, &t);
+    if (st != SPMM_SUCCESS)
+        return st;
+    if (M == 0 || N == 0)
+        return SPMM_SUCCESS;
+    const ScratchLayout lay = scratch_layout(M);
+    if ((size_t)lay.total > kFixedScratchBytes)
+        return fail(SPMM_ERROR_UNSUPPORTED,
+                    "M = " + std::to_string(M) + " needs " + std::to_string(lay.total) +
+                    " bytes of plan scratch; the fixed array of the no-allocation "
+                    "entry point holds " + std::to_string(kFixedScratchBytes) +
+                    " (at most " + std::to_string(fixed_scratch_max_rows()) + " rows)");
+    hipStream_t stream = (hipStream_t)stream_ptr;
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return fail_hip(err, "hipGetDevice");
+    FixedScratch *fs = nullptr;
+    if ((err = fixed_scratch_for(dev, &fs)) != hipSuccess)
+        return fail_hip(err, "hipGetSymbolAddress(scratch)");
+    std::lock_guard<std::mutex> guard(fs->mu);  // until the launch is enqueued
+    if (fs->epoch == UINT32_MAX) {
+        // epochs used up: clear every word, then start again at 1
+        const int64_t words = (int64_t)(kFixedScratchBytes / 8);
+        hipLaunchKernelGGL(zero_fixed_scratch, dim3(1024), dim3(256), 0, stream,
+                           (uint64_t *)fs->ptr, words);
+        if ((err = hipGetLastError()) != hipSuccess)
+            return fail_hip(err, "clearing the fixed scratch");
+        fs->epoch = 0;
+    }
+    WorkerArgs wa;
+    wa.rowptr = rowptr;
+    wa.colind = colind;
+    wa.vals = vals;
+    wa.vals_relative = 0;
+    wa.B = B;
+    wa.C = C;
+    wa.dot_rows = nullptr;
+    wa.dot_cols = nullptr;
+    wa.M = M;
+    wa.K = K;
+    wa.N = N;
+    wa.th.short_max = t.short_max;
+    wa.th.medium_max = t.medium_max;
+    wa.th.chunk_nnz = t.chunk_nnz;
+    wa.plan = carve(fs->ptr, lay);
+    wa.shape = plan_shape(M);
+    wa.epoch = ++fs->epoch;
+    const WorkerConfig cfg = choose_worker(dtype, N, B, C);
+    err = launch_worker(cfg, wa, stream, nullptr, nullptr);
+    if (err != hipSuccess)
+        return fail_hip(err, "worker kernel");
+    return SPMM_SUCCESS;
 }
 
 spmm_status_t launch_sddmm_checked(int32_t dtype, const int32_t *rowptr,
@@ -797,6 +935,15 @@ spmm_status_t spmm_csr_tuned(int32_t dtype, const int32_t *rowptr,
                              void *stream)
 {
     return run(dtype, rowptr, colind, vals, B, C, M, K, N, tuning, stream);
+}
+
+spmm_status_t spmm_csr_tuned_noalloc(int32_t dtype, const int32_t *rowptr,
+                                     const int32_t *colind, const void *vals,
+                                     const void *B, float *C, int64_t M,
+                                     int64_t K, int64_t N,
+                                     const spmm_tuning_t *tuning, void *stream)
+{
+    return run_noalloc(dtype, rowptr, colind, vals, B, C, M, K, N, tuning, stream);
 }
 
 spmm_status_t spmm_resolve_tuning(int32_t dtype, int64_t N,

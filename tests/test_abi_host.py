@@ -29,7 +29,8 @@ def test_header_declares_entry_points():
     for must in ("spmm_csr_f32", "spmm_csr_bf16in_f32acc", "spmm_csr_tuned",
                  "spmm_resolve_tuning", "spmm_plan_export", "spmm_status_string",
                  "spmm_last_error", "spmm_timing_enable", "spmm_timing_read",
-                 "spmm_stream_faults", "spmm_stream_release", "sddmm_csr_f32", "sddmm_csr_bf16in_f32acc",
+                 "spmm_stream_faults", "spmm_stream_release", "spmm_csr_tuned_noalloc",
+                 "sddmm_csr_f32", "sddmm_csr_bf16in_f32acc",
                  "fusedmm_csr_f32", "fusedmm_csr_bf16in_f32acc"):
         assert must in names
 
@@ -117,6 +118,22 @@ def test_tuned_rejects_bad_tuning():
     rc = raw_call("spmm_csr_tuned", 5, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 4,
                   None, None)
     assert rc == 1
+
+
+def test_noalloc_rejects_on_the_host():
+    """The no-allocation entry point checks like spmm_csr_tuned, and rejects
+    an M whose plan does not fit its fixed array, before any HIP call."""
+    rc = raw_call("spmm_csr_tuned_noalloc", 0, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 4, 4,
+                  None, None)
+    assert rc == 1
+    rc = raw_call("spmm_csr_tuned_noalloc", 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 22, 4, 4,
+                  None, None)
+    assert rc == 4
+    msg = sdl.lib().spmm_last_error().decode()
+    assert "at most" in msg and "rows" in msg
+    rc = raw_call("spmm_csr_tuned_noalloc", 0, None, None, None, None, None, 0, 4, 4,
+                  None, None)
+    assert rc == 0                      # M == 0: nothing to do
 
 
 def test_forced_allocation_failure(monkeypatch):
