@@ -88,16 +88,30 @@ typedef int32_t spmm_status_t;
  * entries is
  *   short   if len <= short_max          one sub-wavefront lane group per row
  *   medium  if short_max < len <= medium_max   one wavefront per row
- *   long    if len > medium_max          cut into ceil(len / chunk_nnz)
+ *   long    if medium_max < len <= H     cut into ceil(len / chunk_nnz)
  *                                        near-equal chunks, one wavefront each
- * Fields < 0 (short_max, medium_max) or <= 0 (chunk_nnz) ask for the
- * library's default for the given element type and N.  The thresholds never
- * change C beyond rounding; they only route work.
+ *   hub     if len > H                   cut at column-slab boundaries: chunk
+ *                                        s holds the entries with columns in
+ *                                        [s*slab_rows, (s+1)*slab_rows) (for
+ *                                        ascending columns), one wavefront each
+ * with H = max(hub_min, medium_max).  Hub chunks of neighbouring slabs run on
+ * the same XCD, slab after slab, so the slab's rows of B are gathered from
+ * that XCD's L2 by every hub row that has entries in it ([Multilevel] "Sparse
+ * Matrix-Matrix Multiplication on Multilevel Memory Architectures", the
+ * access-pattern analysis: row j of B is read once per non-zero in column j).
+ * Fields < 0 (short_max, medium_max, hub_min) or <= 0 (chunk_nnz, slab_rows)
+ * ask for the library's default for the given element type, K and N: hub
+ * rows only when B holds at least 256 MiB (more than the Infinity Cache),
+ * slabs of 2 MiB of B's rows, and H at least 32 entries per slab.
+ * hub_min = INT32_MAX turns hub rows off.
+ * The thresholds never change C beyond rounding; they only route work.
  */
 typedef struct spmm_tuning {
     int32_t short_max;
     int32_t medium_max;
     int32_t chunk_nnz;
+    int32_t hub_min;
+    int32_t slab_rows;
     int32_t reserved;   /* must be 0 */
 } spmm_tuning_t;
 
@@ -163,32 +177,41 @@ spmm_status_t spmm_csr_tuned_noalloc(int32_t dtype, const int32_t *rowptr,
                                      const spmm_tuning_t *tuning, void *stream);
 
 /*
- * Host only, no HIP call: the thresholds a call with this dtype, N and
+ * Host only, no HIP call: the thresholds a call with this dtype, K, N and
  * requested tuning (NULL = all defaults) would use, written to *resolved.
  */
-spmm_status_t spmm_resolve_tuning(int32_t dtype, int64_t N,
+spmm_status_t spmm_resolve_tuning(int32_t dtype, int64_t K, int64_t N,
                                   const spmm_tuning_t *requested,
                                   spmm_tuning_t *resolved);
 
 /*
  * Introspection for tests: run only the planning pass on device rowptr
- * (M rows) with the given thresholds, wait for it, and copy the plan to
- * host arrays:
- *   counts[4]          n_short, n_medium, n_long, n_chunks
+ * (M rows; colind of K columns for the hub chunks) with the given resolved
+ * thresholds, wait for it, and copy the plan to host arrays:
+ *   counts[6]          n_short, n_medium, n_long, n_chunks, n_hub,
+ *                      n_hub_chunks (= n_hub * ceil(K / slab_rows))
  *   medium_rows[cap]   ascending rows with short_max < len <= medium_max
  *   long_rows[3*cap]   per long row, ascending: row, first chunk, chunks
  *   chunks[4*cap]      per chunk, ordered by row then position:
  *                      row, first position, end position, long-row index
+ *   hub_rows[cap]      ascending hub rows
+ *   hub_chunks[4*cap]  per hub chunk, slab-major (slab s of hub h at
+ *                      s * n_hub + h): row, first position, end position,
+ *                      hub index; the bounds come from the product's own
+ *                      search over colind
  * Each output array receives at most `cap` records (counts are always
  * complete).  Synchronises `stream`.  The chunk table the worker reads
  * holds M + 4096 records; chunks beyond it are recomputed from long_rows,
- * and this call reports the recomputed values for them as well.
+ * and this call reports the recomputed values for them as well.  colind
+ * may be NULL only when hub_min is INT32_MAX (no hub rows).
  */
-spmm_status_t spmm_plan_export(const int32_t *rowptr, int64_t M,
+spmm_status_t spmm_plan_export(const int32_t *rowptr, const int32_t *colind,
+                               int64_t M, int64_t K,
                                const spmm_tuning_t *resolved, void *stream,
                                int64_t cap, int64_t *counts,
                                int32_t *medium_rows, int32_t *long_rows,
-                               int32_t *chunks);
+                               int32_t *chunks, int32_t *hub_rows,
+                               int32_t *hub_chunks);
 
 /* Static text naming a status code. */
 const char *spmm_status_string(spmm_status_t status);

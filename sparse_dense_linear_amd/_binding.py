@@ -28,7 +28,8 @@ class SpmmError(RuntimeError):
 
 class _TuningStruct(ctypes.Structure):
     _fields_ = [("short_max", ctypes.c_int32), ("medium_max", ctypes.c_int32),
-                ("chunk_nnz", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("chunk_nnz", ctypes.c_int32), ("hub_min", ctypes.c_int32),
+                ("slab_rows", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 @dataclass
@@ -37,9 +38,12 @@ class Tuning:
     short_max: int = -1
     medium_max: int = -1
     chunk_nnz: int = 0
+    hub_min: int = -1
+    slab_rows: int = 0
 
     def _struct(self) -> _TuningStruct:
-        return _TuningStruct(self.short_max, self.medium_max, self.chunk_nnz, 0)
+        return _TuningStruct(self.short_max, self.medium_max, self.chunk_nnz,
+                             self.hub_min, self.slab_rows, 0)
 
 
 _lib = None
@@ -66,10 +70,10 @@ def lib() -> ctypes.CDLL:
                                  ctypes.POINTER(_TuningStruct), P]
     L.spmm_csr_tuned_noalloc.argtypes = [I32, P, P, P, P, P, I64, I64, I64,
                                          ctypes.POINTER(_TuningStruct), P]
-    L.spmm_resolve_tuning.argtypes = [I32, I64, ctypes.POINTER(_TuningStruct),
+    L.spmm_resolve_tuning.argtypes = [I32, I64, I64, ctypes.POINTER(_TuningStruct),
                                       ctypes.POINTER(_TuningStruct)]
-    L.spmm_plan_export.argtypes = [P, I64, ctypes.POINTER(_TuningStruct), P, I64,
-                                   P, P, P, P]
+    L.spmm_plan_export.argtypes = [P, P, I64, I64, ctypes.POINTER(_TuningStruct), P, I64,
+                                   P, P, P, P, P, P]
     L.spmm_status_string.argtypes = [I32]
     L.spmm_status_string.restype = ctypes.c_char_p
     L.spmm_last_error.argtypes = []
@@ -366,43 +370,52 @@ def fusedmm(rowptr, colind, C, B, D, stream=None):
     return E
 
 
-def resolve_tuning(dtype: int, N: int, tuning: Tuning | None = None) -> Tuning:
-    """Thresholds a call with this dtype and N would use (host only)."""
+def resolve_tuning(dtype: int, N: int, tuning: Tuning | None = None, K: int = 0) -> Tuning:
+    """Thresholds a call with this dtype, K and N would use (host only)."""
     out = _TuningStruct()
     ts = None if tuning is None else ctypes.byref(tuning._struct())
-    _check(lib().spmm_resolve_tuning(dtype, N, ts, ctypes.byref(out)),
+    _check(lib().spmm_resolve_tuning(dtype, K, N, ts, ctypes.byref(out)),
            "spmm_resolve_tuning")
-    return Tuning(out.short_max, out.medium_max, out.chunk_nnz)
+    return Tuning(out.short_max, out.medium_max, out.chunk_nnz, out.hub_min, out.slab_rows)
 
 
-def plan_export(rowptr, resolved: Tuning, cap: int | None = None, stream=None) -> dict:
-    """Run only the planning pass on device rowptr and return the plan as
-    numpy arrays (synchronises the stream).  With cap=None the counts are
-    read first and the arrays sized to hold the whole plan."""
+def plan_export(rowptr, resolved: Tuning, colind=None, K: int = 0,
+                cap: int | None = None, stream=None) -> dict:
+    """Run only the planning pass on device rowptr (and colind, for the hub
+    chunks) and return the plan as numpy arrays (synchronises the stream).
+    With cap=None the counts are read first and the arrays sized to hold the
+    whole plan."""
     import numpy as np
     M = rowptr.numel() - 1
-    ts = _TuningStruct(resolved.short_max, resolved.medium_max, resolved.chunk_nnz, 0)
+    ts = resolved._struct()
     handle = _stream_handle(rowptr.device, stream)
-    counts = np.zeros(4, dtype=np.int64)
+    counts = np.zeros(6, dtype=np.int64)
+    cptr = None if colind is None else _ptr(colind)
     if cap is None:
-        _check(lib().spmm_plan_export(_ptr(rowptr), M, ctypes.byref(ts), handle, 0,
-                                      counts.ctypes.data, None, None, None),
+        _check(lib().spmm_plan_export(_ptr(rowptr), cptr, M, K, ctypes.byref(ts), handle, 0,
+                                      counts.ctypes.data, None, None, None, None, None),
                "spmm_plan_export")
         cap = int(counts[1:].max()) if M > 0 else 0
     cap_rows = max(cap, 1)
     medium = np.zeros(cap_rows, dtype=np.int32)
     long_rows = np.zeros((cap_rows, 3), dtype=np.int32)
     chunks = np.zeros((cap_rows, 4), dtype=np.int32)
-    _check(lib().spmm_plan_export(_ptr(rowptr), M, ctypes.byref(ts), handle, cap,
+    hubs = np.zeros(cap_rows, dtype=np.int32)
+    hub_chunks = np.zeros((cap_rows, 4), dtype=np.int32)
+    _check(lib().spmm_plan_export(_ptr(rowptr), cptr, M, K, ctypes.byref(ts), handle, cap,
                                   counts.ctypes.data, medium.ctypes.data,
-                                  long_rows.ctypes.data, chunks.ctypes.data),
+                                  long_rows.ctypes.data, chunks.ctypes.data,
+                                  hubs.ctypes.data, hub_chunks.ctypes.data),
            "spmm_plan_export")
-    n_short, n_med, n_long, n_ch = (int(x) for x in counts)
+    n_short, n_med, n_long, n_ch, n_hub, n_hch = (int(x) for x in counts)
     return {
         "n_short": n_short, "n_medium": n_med, "n_long": n_long, "n_chunks": n_ch,
+        "n_hub": n_hub, "n_hub_chunks": n_hch,
         "medium_rows": medium[:min(n_med, cap)],
         "long_rows": long_rows[:min(n_long, cap)],
         "chunks": chunks[:min(n_ch, cap)],
+        "hub_rows": hubs[:min(n_hub, cap)],
+        "hub_chunks": hub_chunks[:min(n_hch, cap)],
     }
 
 

@@ -45,13 +45,27 @@ constexpr int64_t kMaxIndex = (int64_t)1 << 31;  // int32 rows / columns
 // Gathers a lane keeps in flight for a worker variant (see worker.hip).
 int unroll_of(int nv) { return nv == 1 ? 8 : (nv == 2 ? 4 : 2); }
 
-spmm_status_t resolve(int32_t dtype, int64_t N, const spmm_tuning_t *req,
+// Hub rows: used when B is larger than the 256 MB Infinity Cache
+// (kHubMinBBytes); a slab holds kSlabBytes of B's rows, and a row is a hub
+// row when it has at least kHubEntriesPerSlab entries per slab on average
+// (so a hub chunk is worth its search and its atomic adds).  Measured: the
+// skewed 1 GiB-B workload 17.8 -> 6.9 ms (hub threshold 8192-16384 and 2 MiB
+// slabs best; 1 and 4 MiB slabs 7-11 % slower); on the power-law workload
+// (64 MiB B, which the Infinity Cache holds) hub rows gained nothing and
+// varied more from call to call, so below 256 MiB they stay off.
+constexpr int64_t kHubMinBBytes = (int64_t)256 << 20;
+constexpr int64_t kSlabBytes = (int64_t)2 << 20;
+constexpr int64_t kHubEntriesPerSlab = 32;
+
+spmm_status_t resolve(int32_t dtype, int64_t K, int64_t N, const spmm_tuning_t *req,
                       spmm_tuning_t *out)
 {
     if (dtype != SPMM_DTYPE_F32 && dtype != SPMM_DTYPE_BF16)
         return fail(SPMM_ERROR_INVALID_VALUE, "unknown dtype");
     if (N < 0 || N >= kMaxIndex)
         return fail(SPMM_ERROR_INVALID_VALUE, "N out of range");
+    if (K < 0 || K >= kMaxIndex)
+        return fail(SPMM_ERROR_INVALID_VALUE, "K out of range");
     if (req && req->reserved != 0)
         return fail(SPMM_ERROR_INVALID_VALUE, "spmm_tuning_t.reserved must be 0");
     // Nominal variant for this N (aligned pointers): R groups of G lanes.
@@ -71,6 +85,12 @@ spmm_status_t resolve(int32_t dtype, int64_t N, const spmm_tuning_t *req,
     t.short_max = 2 * U;
     t.chunk_nnz = (int32_t)chunk;
     t.medium_max = (int32_t)chunk;
+    const int64_t esz = dtype == SPMM_DTYPE_BF16 ? 2 : 4;
+    const int64_t row_bytes = (N > 0 ? N : 1) * esz;
+    int64_t slab = kSlabBytes / row_bytes;
+    slab = slab < 1 ? 1 : (slab > kMaxIndex - 1 ? kMaxIndex - 1 : slab);
+    t.slab_rows = (int32_t)slab;
+    t.hub_min = INT32_MAX;   // no hub rows
     t.reserved = 0;
     if (req) {
         if (req->short_max >= 0)
@@ -79,7 +99,17 @@ spmm_status_t resolve(int32_t dtype, int64_t N, const spmm_tuning_t *req,
             t.medium_max = req->medium_max;
         if (req->chunk_nnz > 0)
             t.chunk_nnz = req->chunk_nnz;
+        if (req->slab_rows > 0)
+            t.slab_rows = req->slab_rows;
     }
+    if (K * row_bytes >= kHubMinBBytes) {
+        const int64_t n_slabs = (K + t.slab_rows - 1) / t.slab_rows;
+        int64_t h = kHubEntriesPerSlab * n_slabs;
+        h = h < t.medium_max ? t.medium_max : (h > INT32_MAX ? INT32_MAX : h);
+        t.hub_min = (int32_t)h;
+    }
+    if (req && req->hub_min >= 0)
+        t.hub_min = req->hub_min;
     // A short tile stages at most kShortCap entries and holds at least R
     // rows, so a short row may hold at most kShortCap / R entries; longer
     // rows go to the medium kind.
@@ -89,6 +119,19 @@ spmm_status_t resolve(int32_t dtype, int64_t N, const spmm_tuning_t *req,
         return fail(SPMM_ERROR_INVALID_VALUE, "short_max > medium_max");
     *out = t;
     return SPMM_SUCCESS;
+}
+
+// The kernels' form of resolved thresholds for a call with K rows of B.
+Thresholds thresholds_of(const spmm_tuning_t &t, int64_t K)
+{
+    Thresholds th;
+    th.short_max = t.short_max;
+    th.medium_max = t.medium_max;
+    th.chunk_nnz = t.chunk_nnz;
+    th.hub_top = t.hub_min > t.medium_max ? t.hub_min : t.medium_max;
+    th.slab_rows = t.slab_rows;
+    th.n_slabs = (int32_t)((K + t.slab_rows - 1) / t.slab_rows);
+    return th;
 }
 
 // ------------------------------------------------------------- scratch
@@ -137,20 +180,22 @@ struct ScratchLayout {
     int64_t counts, faults, queues, agg, medium_rows, long_row,
         long_first, chunk_row, chunk_k, total;
     int64_t chunk_cap;
+    int64_t rows;
 };
 
 ScratchLayout scratch_layout(int64_t M)
 {
     ScratchLayout l;
+    l.rows = M;
     int64_t off = 0;
     l.counts = off;
-    off = align_up(off + 4 * 8, 256);
+    off = align_up(off + 5 * 8, 256);
     l.faults = off;
     off = align_up(off + 4, 256);
     l.queues = off;
     off = align_up(off + 4 * 2 * kQueues * kQueueStride, 256);
     l.agg = off;
-    off = align_up(off + 8 * 3 * kPlanMaxBlocks, 256);
+    off = align_up(off + 8 * kPlanCounts * kPlanMaxBlocks, 256);
     l.medium_rows = off;
     off = align_up(off + 8 * M, 256);
     l.long_row = off;
@@ -179,6 +224,7 @@ PlanBuffers carve(char *base, const ScratchLayout &l)
     b.faults = (uint32_t *)(base + l.faults);
     b.queues = (uint32_t *)(base + l.queues);
     b.chunk_cap = l.chunk_cap;
+    b.rows = l.rows;
     return b;
 }
 
@@ -442,7 +488,7 @@ spmm_status_t run_with(int32_t dtype, const int32_t *rowptr,
     if (st != SPMM_SUCCESS)
         return st;
     spmm_tuning_t t;
-    st = resolve(dtype, N, tuning, &t);
+    st = resolve(dtype, K, N, tuning, &t);
     if (st != SPMM_SUCCESS)
         return st;
     if (M == 0 || N == 0)
@@ -498,9 +544,7 @@ spmm_status_t run_with(int32_t dtype, const int32_t *rowptr,
     wa.M = M;
     wa.K = K;
     wa.N = N;
-    wa.th.short_max = t.short_max;
-    wa.th.medium_max = t.medium_max;
-    wa.th.chunk_nnz = t.chunk_nnz;
+    wa.th = thresholds_of(t, K);
     wa.plan = carve((char *)scratch, lay);
     wa.shape = plan_shape(M);
     wa.epoch = epoch;
@@ -537,7 +581,7 @@ spmm_status_t run_noalloc(int32_t dtype, const int32_t *rowptr,
     if (st != SPMM_SUCCESS)
         return st;
     spmm_tuning_t t;
-    st = resolve(dtype, N, tuning, &t);
+    st = resolve(dtype, K, N, tuning, &t);
     if (st != SPMM_SUCCESS)
         return st;
     if (M == 0 || N == 0)
@@ -579,9 +623,7 @@ spmm_status_t run_noalloc(int32_t dtype, const int32_t *rowptr,
     wa.M = M;
     wa.K = K;
     wa.N = N;
-    wa.th.short_max = t.short_max;
-    wa.th.medium_max = t.medium_max;
-    wa.th.chunk_nnz = t.chunk_nnz;
+    wa.th = thresholds_of(t, K);
     wa.plan = carve(fs->ptr, lay);
     wa.shape = plan_shape(M);
     wa.epoch = ++fs->epoch;
@@ -946,38 +988,44 @@ spmm_status_t spmm_csr_tuned_noalloc(int32_t dtype, const int32_t *rowptr,
     return run_noalloc(dtype, rowptr, colind, vals, B, C, M, K, N, tuning, stream);
 }
 
-spmm_status_t spmm_resolve_tuning(int32_t dtype, int64_t N,
+spmm_status_t spmm_resolve_tuning(int32_t dtype, int64_t K, int64_t N,
                                   const spmm_tuning_t *requested,
                                   spmm_tuning_t *resolved)
 {
     g_last_error.clear();
     if (resolved == nullptr)
         return fail(SPMM_ERROR_INVALID_VALUE, "resolved is null");
-    return resolve(dtype, N, requested, resolved);
+    return resolve(dtype, K, N, requested, resolved);
 }
 
-spmm_status_t spmm_plan_export(const int32_t *rowptr, int64_t M,
+spmm_status_t spmm_plan_export(const int32_t *rowptr, const int32_t *colind,
+                               int64_t M, int64_t K,
                                const spmm_tuning_t *resolved, void *stream_ptr,
                                int64_t cap, int64_t *counts,
                                int32_t *medium_rows, int32_t *long_rows,
-                               int32_t *chunks)
+                               int32_t *chunks, int32_t *hub_rows,
+                               int32_t *hub_chunks)
 {
     g_last_error.clear();
     if (resolved == nullptr || counts == nullptr)
         return fail(SPMM_ERROR_INVALID_VALUE, "null argument");
     if (resolved->short_max < 0 || resolved->medium_max < resolved->short_max ||
-        resolved->chunk_nnz <= 0 || resolved->reserved != 0)
+        resolved->chunk_nnz <= 0 || resolved->hub_min < 0 ||
+        resolved->slab_rows <= 0 || resolved->reserved != 0)
         return fail(SPMM_ERROR_INVALID_VALUE, "tuning must be fully resolved");
-    if (M < 0 || M >= kMaxIndex || cap < 0)
-        return fail(SPMM_ERROR_INVALID_VALUE, "M or cap out of range");
-    if (cap > 0 && (medium_rows == nullptr || long_rows == nullptr || chunks == nullptr))
+    if (M < 0 || M >= kMaxIndex || K < 0 || K >= kMaxIndex || cap < 0)
+        return fail(SPMM_ERROR_INVALID_VALUE, "M, K or cap out of range");
+    if (cap > 0 && (medium_rows == nullptr || long_rows == nullptr || chunks == nullptr ||
+                    hub_rows == nullptr || hub_chunks == nullptr))
         return fail(SPMM_ERROR_INVALID_VALUE, "null output array");
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 6; ++q)
         counts[q] = 0;
     if (M == 0)
         return SPMM_SUCCESS;
     if (rowptr == nullptr)
         return fail(SPMM_ERROR_INVALID_VALUE, "rowptr is null");
+    if (colind == nullptr && resolved->hub_min < INT32_MAX)
+        return fail(SPMM_ERROR_INVALID_VALUE, "colind is null (hub chunks need it)");
 
     hipStream_t stream = (hipStream_t)stream_ptr;
     const ScratchLayout lay = scratch_layout(M);
@@ -987,8 +1035,10 @@ spmm_status_t spmm_plan_export(const int32_t *rowptr, int64_t M,
     const int64_t off_med = align_up(lay.total, 256);
     const int64_t off_long = align_up(off_med + 4 * recs, 256);
     const int64_t off_chunk = align_up(off_long + (int64_t)sizeof(LongRow) * recs, 256);
-    const int64_t off_counts = align_up(off_chunk + (int64_t)sizeof(Chunk) * recs, 256);
-    const int64_t total = off_counts + 4 * 8;
+    const int64_t off_hub = align_up(off_chunk + (int64_t)sizeof(Chunk) * recs, 256);
+    const int64_t off_hchunk = align_up(off_hub + 4 * recs, 256);
+    const int64_t off_counts = align_up(off_hchunk + (int64_t)sizeof(Chunk) * recs, 256);
+    const int64_t total = off_counts + 6 * 8;
     hipError_t err = hipMalloc(&dev_mem, (size_t)total);
     if (err != hipSuccess)
         return fail_hip(err, "hipMalloc");
@@ -1001,22 +1051,24 @@ spmm_status_t spmm_plan_export(const int32_t *rowptr, int64_t M,
         WorkerArgs wa;
         memset(&wa, 0, sizeof wa);
         wa.rowptr = rowptr;
+        wa.colind = colind;
         wa.M = M;
+        wa.K = K;
         wa.N = 1;
-        wa.th.short_max = resolved->short_max;
-        wa.th.medium_max = resolved->medium_max;
-        wa.th.chunk_nnz = resolved->chunk_nnz;
+        wa.th = thresholds_of(*resolved, K);
         wa.plan = carve(dev_mem, lay);
         wa.shape = plan_shape(M);
         wa.epoch = 1;
         wa.C = nullptr;  // plan only
         const WorkerConfig cfg = choose_worker(SPMM_DTYPE_F32, 1, nullptr, nullptr);
-        int64_t dcounts[4];
+        int64_t dcounts[6];
         if ((err = launch_worker(cfg, wa, stream, nullptr, nullptr)) != hipSuccess ||
-            (err = launch_plan_export(rowptr, M, wa.th, wa.plan, 1, cap,
+            (err = launch_plan_export(rowptr, colind, M, wa.th, wa.plan, 1, cap,
                                       (int32_t *)(dev_mem + off_med),
                                       (LongRow *)(dev_mem + off_long),
                                       (Chunk *)(dev_mem + off_chunk),
+                                      (int32_t *)(dev_mem + off_hub),
+                                      (Chunk *)(dev_mem + off_hchunk),
                                       (int64_t *)(dev_mem + off_counts), stream)) != hipSuccess ||
             (err = hipStreamSynchronize(stream)) != hipSuccess ||
             (err = hipMemcpy(dcounts, dev_mem + off_counts, sizeof dcounts,
@@ -1024,11 +1076,13 @@ spmm_status_t spmm_plan_export(const int32_t *rowptr, int64_t M,
             st = fail_hip(err, "plan");
             break;
         }
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 6; ++q)
             counts[q] = dcounts[q];
         const int64_t nm = dcounts[1] < cap ? dcounts[1] : cap;
         const int64_t nl = dcounts[2] < cap ? dcounts[2] : cap;
         const int64_t nc = dcounts[3] < cap ? dcounts[3] : cap;
+        const int64_t nh = dcounts[4] < cap ? dcounts[4] : cap;
+        const int64_t nhc = dcounts[5] < cap ? dcounts[5] : cap;
         if ((nm > 0 && (err = hipMemcpy(medium_rows, dev_mem + off_med, 4 * nm,
                                         hipMemcpyDeviceToHost)) != hipSuccess) ||
             (nl > 0 && (err = hipMemcpy(long_rows, dev_mem + off_long,
@@ -1036,7 +1090,12 @@ spmm_status_t spmm_plan_export(const int32_t *rowptr, int64_t M,
                                         hipMemcpyDeviceToHost)) != hipSuccess) ||
             (nc > 0 && (err = hipMemcpy(chunks, dev_mem + off_chunk,
                                         sizeof(Chunk) * nc,
-                                        hipMemcpyDeviceToHost)) != hipSuccess)) {
+                                        hipMemcpyDeviceToHost)) != hipSuccess) ||
+            (nh > 0 && (err = hipMemcpy(hub_rows, dev_mem + off_hub, 4 * nh,
+                                        hipMemcpyDeviceToHost)) != hipSuccess) ||
+            (nhc > 0 && (err = hipMemcpy(hub_chunks, dev_mem + off_hchunk,
+                                         sizeof(Chunk) * nhc,
+                                         hipMemcpyDeviceToHost)) != hipSuccess)) {
             st = fail_hip(err, "copy plan");
             break;
         }

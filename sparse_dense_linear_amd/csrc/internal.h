@@ -27,11 +27,16 @@ constexpr int kQueueStride = 64;
 // rows always fits.
 constexpr int kShortCap = 512;
 
-// Routing thresholds, already resolved (see spmm_tuning_t).
+// Routing thresholds, already resolved (see spmm_tuning_t).  Rows with
+// more than hub_top entries are hub rows (hub_top >= medium_max; INT32_MAX:
+// none), cut into n_slabs chunks at multiples of slab_rows columns.
 struct Thresholds {
     int32_t short_max;
     int32_t medium_max;
     int32_t chunk_nnz;
+    int32_t hub_top;     // max(hub_min, medium_max)
+    int32_t slab_rows;   // rows of B per column slab (>= 1)
+    int32_t n_slabs;     // ceil(K / slab_rows) (0 when K == 0)
 };
 
 // Shape of the plan over M rows: n_tiles wavefront tiles of tile_rows rows
@@ -51,10 +56,13 @@ PlanShape plan_shape(int64_t M);
 // scratch is zeroed when it is created, so no word needs clearing between
 // calls.
 struct PlanBuffers {
-    uint64_t *counts;        // [4] n_medium, n_long, n_chunks, n_short
-    uint64_t *agg;           // [3][kPlanMaxBlocks] per plan block: medium, long, chunks
+    uint64_t *counts;        // [5] n_medium, n_long, n_chunks, n_short, n_hub
+    uint64_t *agg;           // [4][kPlanMaxBlocks] per plan block: medium, long,
+                             // chunks, hubs
     uint64_t *medium_rows;   // [M] rows with short_max < len <= medium_max
-    uint64_t *long_row;      // [M] long rows, ascending
+    uint64_t *long_row;      // [M] long rows, ascending, from the front; hub
+                             // row l (ascending) at long_row[M - 1 - l] (the
+                             // two lists together hold at most M rows)
     uint64_t *long_first;    // [M] index of each long row's first chunk
     uint64_t *chunk_row;     // [chunk_cap] row of each chunk
     uint64_t *chunk_k;       // [chunk_cap] position of the chunk in its row
@@ -64,7 +72,10 @@ struct PlanBuffers {
                              // takes an epoch (product or element-balanced)
                              // clears set (epoch + 1) & 1 (not tagged)
     int64_t chunk_cap;       // M + kChunkTableSlack
+    int64_t rows;            // M: hub row l is long_row[rows - 1 - l]
 };
+
+constexpr int kPlanCounts = 4;   // per plan block: medium, long, chunks, hubs
 
 // Bounds of chunk k of a long row that starts at `start`, holds `len`
 // entries and is cut into n chunks: positions
@@ -192,12 +203,16 @@ struct Chunk {
 
 // Copy the tagged plan of a finished plan-only launch into plain device
 // arrays (at most `cap` records each; a record whose word does not carry
-// `epoch` is written as -1).  counts_out[4] gets n_short, n_medium, n_long,
-// n_chunks.  Enqueued on `stream`.
-hipError_t launch_plan_export(const int32_t *rowptr, int64_t M, Thresholds th,
+// `epoch` is written as -1).  counts_out[6] gets n_short, n_medium, n_long,
+// n_chunks, n_hub, n_hub * n_slabs; hub chunks in item order (slab-major),
+// their bounds found by the product's own search over colind.  Enqueued on
+// `stream`.
+hipError_t launch_plan_export(const int32_t *rowptr, const int32_t *colind,
+                              int64_t M, Thresholds th,
                               const PlanBuffers &pb, uint32_t epoch,
                               int64_t cap, int32_t *medium_out,
                               LongRow *long_out, Chunk *chunk_out,
+                              int32_t *hub_out, Chunk *hub_chunk_out,
                               int64_t *counts_out, hipStream_t stream);
 
 }  // namespace sdl

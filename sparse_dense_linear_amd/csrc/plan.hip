@@ -54,22 +54,27 @@ __device__ inline int32_t untag(uint64_t w, uint32_t epoch)
 __global__ __launch_bounds__(kExportBlock) void plan_export_kernel(
     const int32_t *__restrict__ rowptr, int64_t M, Thresholds th,
     PlanBuffers pb, uint32_t epoch, int64_t cap, int32_t *medium_out,
-    LongRow *long_out, Chunk *chunk_out, int64_t *counts_out)
+    LongRow *long_out, Chunk *chunk_out, int32_t *hub_out, int64_t *counts_out)
 {
     const int64_t n_med = untag(pb.counts[0], epoch);
     const int64_t n_long = untag(pb.counts[1], epoch);
     const int64_t n_ch = untag(pb.counts[2], epoch);
+    const int64_t n_hub = untag(pb.counts[4], epoch);
     const int64_t i = (int64_t)blockIdx.x * kExportBlock + threadIdx.x;
     if (i == 0) {
         counts_out[0] = untag(pb.counts[3], epoch);
         counts_out[1] = n_med;
         counts_out[2] = n_long;
         counts_out[3] = n_ch;
+        counts_out[4] = n_hub;
+        counts_out[5] = n_hub < 0 ? -1 : n_hub * th.n_slabs;
     }
     if (i >= cap)
         return;
     if (i < n_med)
         medium_out[i] = untag(pb.medium_rows[i], epoch);
+    if (i < n_hub)
+        hub_out[i] = untag(*hub_slot(pb, i), epoch);
     if (i < n_long) {
         LongRow lr;
         lr.row = untag(pb.long_row[i], epoch);
@@ -115,6 +120,34 @@ __global__ __launch_bounds__(kExportBlock) void plan_export_kernel(
     }
 }
 
+// Hub chunks in item order (slab-major), one wavefront each, bounds found
+// by the same search the product uses (slab_bounds).
+__global__ __launch_bounds__(kExportBlock) void hub_chunk_export_kernel(
+    const int32_t *__restrict__ rowptr, const int32_t *__restrict__ colind,
+    Thresholds th, PlanBuffers pb, uint32_t epoch, int64_t cap, Chunk *out)
+{
+    const int64_t c = (int64_t)blockIdx.x * (kExportBlock / kWave) + threadIdx.x / kWave;
+    const int64_t n_hub = untag(pb.counts[4], epoch);
+    if (n_hub <= 0 || c >= cap || c >= n_hub * th.n_slabs)
+        return;
+    const int64_t s = c / n_hub, l = c - s * n_hub;
+    Chunk ch;
+    ch.long_idx = (int32_t)l;
+    ch.row = untag(*hub_slot(pb, l), epoch);
+    ch.p0 = ch.p1 = -1;
+    if (ch.row >= 0) {
+        const int64_t start = rowptr[ch.row], end = rowptr[ch.row + 1];
+        const int64_t t0 = s * (int64_t)th.slab_rows, t1 = t0 + th.slab_rows;
+        int64_t p0, p1;
+        slab_bounds(colind, start, end, (int32_t)(t0 < INT32_MAX ? t0 : INT32_MAX),
+                    (int32_t)(t1 < INT32_MAX ? t1 : INT32_MAX), &p0, &p1);
+        ch.p0 = (int32_t)(s == 0 ? start : p0);
+        ch.p1 = (int32_t)(s + 1 >= th.n_slabs ? end : p1);
+    }
+    if ((threadIdx.x & (kWave - 1)) == 0)
+        out[c] = ch;
+}
+
 }  // namespace
 
 hipError_t launch_call(const WorkerConfig &cfg, const WorkerArgs &a,
@@ -132,18 +165,27 @@ hipError_t launch_worker(const WorkerConfig &cfg, const WorkerArgs &a,
     return hipGetLastError();
 }
 
-hipError_t launch_plan_export(const int32_t *rowptr, int64_t M, Thresholds th,
+hipError_t launch_plan_export(const int32_t *rowptr, const int32_t *colind,
+                              int64_t M, Thresholds th,
                               const PlanBuffers &pb, uint32_t epoch,
                               int64_t cap, int32_t *medium_out,
                               LongRow *long_out, Chunk *chunk_out,
+                              int32_t *hub_out, Chunk *hub_chunk_out,
                               int64_t *counts_out, hipStream_t stream)
 {
-    (void)M;
     const int64_t n = cap > 1 ? cap : 1;
     const int64_t blocks = (n + kExportBlock - 1) / kExportBlock;
     hipLaunchKernelGGL(plan_export_kernel, dim3((unsigned)blocks),
                        dim3(kExportBlock), 0, stream, rowptr, M, th, pb, epoch,
-                       cap, medium_out, long_out, chunk_out, counts_out);
+                       cap, medium_out, long_out, chunk_out, hub_out, counts_out);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || cap == 0 || colind == nullptr)
+        return err;
+    const int64_t waves_per_block = kExportBlock / kWave;
+    const int64_t hblocks = (cap + waves_per_block - 1) / waves_per_block;
+    hipLaunchKernelGGL(hub_chunk_export_kernel, dim3((unsigned)hblocks),
+                       dim3(kExportBlock), 0, stream, rowptr, colind, th, pb, epoch,
+                       cap, hub_chunk_out);
     return hipGetLastError();
 }
 

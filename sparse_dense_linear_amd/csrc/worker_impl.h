@@ -29,8 +29,12 @@
 //     through LDS (staged with their rows) for a short tile.
 //   * One launch per call: the first workgroups compute the plan
 //     (plan_device.h) while the others start on short tiles; then every
-//     wavefront takes items from 64 work queues (see call_kernel).  Three
+//     wavefront takes items from 64 work queues (see call_kernel).  Four
 //     kinds of work item:
+//       hub chunk   the entries of a hub row (the longest rows) whose
+//                   columns fall in one slab of B's rows; each XCD takes the
+//                   chunks of its own range of slabs, slab after slab, so
+//                   they gather from its L2; added into C with atomics;
 //       long chunk  (row, p0, p1) from the plan: the R groups split the
 //                   chunk's entries, their partial rows are summed by
 //                   butterfly shuffles, and group 0 adds the result to C
@@ -158,11 +162,45 @@ __device__ inline bool medium_ready(const WorkerArgs &a, int64_t i, int64_t *row
     return true;
 }
 
+// Add one column pass of a row's partial sums into C with device atomics.
+// After reduce_groups every group holds the sums; group 0 lays each of its
+// vectors out in the wavefront's LDS area in column order, and then all 64
+// lanes add 64 consecutive floats per instruction, so each atomic
+// instruction covers whole 256-byte spans of the row (adding straight from
+// the lanes' vectors would touch one float per 16 bytes per instruction and
+// send every float to memory in a separate sector).
+template <class S>
+__device__ inline void add_row_atomic(WaveStage &ws, float *C, int64_t row,
+                                      int64_t N, int64_t col0, int g, int j,
+                                      int lane, const float (&acc)[S::NV][S::VEC])
+{
+    float *f = reinterpret_cast<float *>(ws.ent);   // G * VEC <= 512 floats
+    float *crow = C + row * N + col0;
+    const int64_t left = N - col0;                  // columns of the pass
+#pragma unroll
+    for (int k = 0; k < S::NV; ++k) {
+        const int64_t cbase = (int64_t)k * S::G * S::VEC;   // vector k's columns
+        if (cbase >= left)
+            break;
+        __builtin_amdgcn_wave_barrier();   // earlier reads of the area are done
+        if (g == 0) {
+#pragma unroll
+            for (int x = 0; x < S::VEC; ++x)
+                f[j * S::VEC + x] = acc[k][x];
+        }
+        __builtin_amdgcn_wave_barrier();   // the vectors are in place
+        for (int c = lane; c < S::G * S::VEC; c += kWave)
+            if (cbase + c < left)
+                unsafeAtomicAdd(crow + cbase + c, f[c]);
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
 // One wavefront accumulates row `row` over positions [p0, p1) and stores
-// (medium row) or atomically adds (long-row chunk) the result.
+// (medium row) or atomically adds (long-row or hub chunk) the result.
 template <class S, bool ATOMIC>
-__device__ void do_range(const WorkerArgs &a, int lane, int g, int j,
-                         int64_t row, int64_t p0, int64_t p1,
+__device__ void do_range(const WorkerArgs &a, WaveStage &ws, int lane, int g,
+                         int j, int64_t row, int64_t p0, int64_t p1,
                          const BSrc &src, const BSrc &ysrc, uint32_t row_bytes)
 {
     for (int64_t col0 = 0; col0 < a.N; col0 += S::COLS) {
@@ -170,8 +208,10 @@ __device__ void do_range(const WorkerArgs &a, int lane, int g, int j,
         float acc[S::NV][S::VEC];
         wave_range<S>(a, lane, g, row, p0, p1, src, ysrc, lc, row_bytes, acc);
         reduce_groups<S>(acc);
-        if (g == 0)
-            emit_row<S, ATOMIC>(a.C, row, a.N, col0, j, acc);
+        if constexpr (ATOMIC)
+            add_row_atomic<S>(ws, a.C, row, a.N, col0, g, j, lane, acc);
+        else if (g == 0)
+            emit_row<S, false>(a.C, row, a.N, col0, j, acc);
     }
 }
 
@@ -325,16 +365,29 @@ __device__ inline int64_t xcd_logical_block(int64_t b, int64_t nb)
 
 // Plan totals if this call's have been published (no waiting).
 __device__ inline bool counts_ready(const WorkerArgs &a, int64_t *n_med,
-                                    int64_t *n_long, int64_t *n_ch)
+                                    int64_t *n_long, int64_t *n_ch, int64_t *n_hub)
 {
     const uint64_t w0 = __shfl(tag_load(a.plan.counts + 0), 0);
     const uint64_t w1 = __shfl(tag_load(a.plan.counts + 1), 0);
     const uint64_t w2 = __shfl(tag_load(a.plan.counts + 2), 0);
-    if (!tag_is(w0, a.epoch) || !tag_is(w1, a.epoch) || !tag_is(w2, a.epoch))
+    const uint64_t w4 = __shfl(tag_load(a.plan.counts + 4), 0);
+    if (!tag_is(w0, a.epoch) || !tag_is(w1, a.epoch) || !tag_is(w2, a.epoch) ||
+        !tag_is(w4, a.epoch))
         return false;
     *n_med = (uint32_t)w0;
     *n_long = (uint32_t)w1;
     *n_ch = (uint32_t)w2;
+    *n_hub = (uint32_t)w4;
+    return true;
+}
+
+// Row of hub l if published.  Never waits.
+__device__ inline bool hub_ready(const WorkerArgs &a, int64_t l, int64_t *row)
+{
+    const uint64_t w = __shfl(tag_load(hub_slot(a.plan, l)), 0);
+    if (!tag_is(w, a.epoch))
+        return false;
+    *row = (uint32_t)w;
     return true;
 }
 
@@ -395,7 +448,7 @@ __device__ inline void do_item(const WorkerArgs &a, const ProductShape &ps,
         // chunk was published; the atomic adds address it through the
         // published row, so they come after the clearing.
         if (wait_for([&]() { return chunk_ready(a, d, n_long, &row, &p0, &p1); }))
-            do_range<S, true>(a, lane, g, j, row, p0, p1, src, ysrc, row_bytes);
+            do_range<S, true>(a, ws, lane, g, j, row, p0, p1, src, ysrc, row_bytes);
         else
             note_fault(a, lane);
     } else {
@@ -405,7 +458,7 @@ __device__ inline void do_item(const WorkerArgs &a, const ProductShape &ps,
         const int64_t m = S::FUSED ? e : e - ps.n_dyn_tiles;
         if (m >= 0 && m < n_med) {
             if (wait_for([&]() { return medium_ready(a, m, &row); }))
-                do_range<S, false>(a, lane, g, j, row, a.rowptr[row],
+                do_range<S, false>(a, ws, lane, g, j, row, a.rowptr[row],
                                    a.rowptr[row + 1], src, ysrc, row_bytes);
             else
                 note_fault(a, lane);
@@ -418,16 +471,48 @@ __device__ inline void do_item(const WorkerArgs &a, const ProductShape &ps,
     }
 }
 
+// Hub chunk c = s * n_hub + l: the entries of hub row l whose columns lie
+// in slab s, [s * slab_rows, (s + 1) * slab_rows) -- found by slab_bounds
+// on the row's columns -- added into the row (cleared by the plan) with
+// atomics.  Hub chunks of neighbouring slabs go to the same XCD (see
+// call_kernel), so the rows of B one slab holds are gathered from that
+// XCD's L2 by all the hubs' chunks of the slab.
+template <class S>
+__device__ inline void do_hub(const WorkerArgs &a, WaveStage &ws, int lane,
+                              int g, int j, int64_t c, int64_t n_hub,
+                              const BSrc &src, const BSrc &ysrc, uint32_t row_bytes)
+{
+    const int64_t s = c / n_hub, l = c - s * n_hub;
+    int64_t row = 0;
+    if (!wait_for([&]() { return hub_ready(a, l, &row); })) {
+        note_fault(a, lane);
+        return;
+    }
+    const int64_t start = a.rowptr[row], end = a.rowptr[row + 1];
+    const int64_t ns = a.th.n_slabs;
+    const int64_t t0 = s * (int64_t)a.th.slab_rows, t1 = t0 + a.th.slab_rows;
+    int64_t p0, p1;
+    slab_bounds(a.colind, start, end, (int32_t)(t0 < INT32_MAX ? t0 : INT32_MAX),
+                (int32_t)(t1 < INT32_MAX ? t1 : INT32_MAX), &p0, &p1);
+    if (s == 0)
+        p0 = start;
+    if (s + 1 >= ns)
+        p1 = end;
+    if (p1 > p0)
+        do_range<S, true>(a, ws, lane, g, j, row, p0, p1, src, ysrc, row_bytes);
+}
+
 // One launch per call, sized to the workgroups that fit at once.
 // Workgroups [0, plan_blocks) first compute the plan (plan_device.h);
 // [plan_blocks, plan_grid) pad that part to a multiple of the 8 XCDs.
 // Product workgroups (the rest) start with one short tile each (static:
 // logical product wavefront w takes tile w, for w < first), which needs no
 // plan.  Then every wavefront, the planners included, takes the remaining
-// items from kQueues work queues: queue q hands out items q, q + kQueues,
-// ... of the list [long-row chunks | short tiles | medium rows], so every
-// queue holds the same mix, and a wavefront that started late or drew slow
-// items simply takes fewer.
+// items from kQueues work queues: queue q first hands out its XCD's hub
+// chunks (see below), then items q, q + kQueues, ... of the list
+// [long-row chunks | short tiles | medium rows], so every queue holds the
+// same mix, and a wavefront that started late or drew slow items simply
+// takes fewer.
 template <class S>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(S::MIN_WAVES)))
 void call_kernel(WorkerArgs a, ProductShape ps)
@@ -497,10 +582,10 @@ void call_kernel(WorkerArgs a, ProductShape ps)
                              ps.passes, src, ysrc, row_bytes);
     }
 
-    int64_t n_med = 0, n_long = 0, n_ch = 0;
-    if (!wait_for([&]() { return counts_ready(a, &n_med, &n_long, &n_ch); })) {
+    int64_t n_med = 0, n_long = 0, n_ch = 0, n_hub = 0;
+    if (!wait_for([&]() { return counts_ready(a, &n_med, &n_long, &n_ch, &n_hub); })) {
         note_fault(a, lane);
-        n_med = n_long = n_ch = 0;
+        n_med = n_long = n_ch = n_hub = 0;
     }
     const int64_t n_dyn = n_ch + n_med + ps.n_dyn_tiles;
     // One item per grab: consecutive items go to different wavefronts at
@@ -509,18 +594,38 @@ void call_kernel(WorkerArgs a, ProductShape ps)
     // together).  Grabs are device atomics on kQueues counters.
     const int64_t q = gw % kQueues;
     uint32_t *ctr = a.plan.queues + ((a.epoch & 1) * kQueues + q) * kQueueStride;
+    // Hub chunks come first and stay on one XCD per slab range: the waves
+    // of queue q belong to blocks q/4 mod 16, which run on XCD x = (q/4) mod
+    // 8 (blocks go to the XCDs round-robin), and XCD x's 8 queues (index k)
+    // hand out the hub chunks of slabs [x*ns/8, (x+1)*ns/8) slab by slab:
+    // chunk s_lo*n_hub + k + 8i is the queue's i-th.  So each XCD sweeps its
+    // own eighth of B's rows, one slab at a time, for all hubs.
+    const int64_t ns = a.th.n_slabs;
+    const int x = (int)((q >> 2) & 7);
+    const int k = (int)(((q >> 5) << 2) | (q & 3));
+    const int64_t s_lo = (int64_t)x * ns / 8, s_hi = (int64_t)(x + 1) * ns / 8;
+    const int64_t hub_base = s_lo * n_hub + k;
+    const int64_t n_xh = (s_hi - s_lo) * n_hub;          // the XCD's hub chunks
+    const int64_t n_qh = n_xh > k ? (n_xh - k + 7) / 8 : 0;  // this queue's
     // Lane 0 holds the next grabbed index; it is read (and waited for) only
     // at the top of the next round, so the grab overlaps the current item.
     uint32_t next = 0;
     if (lane == 0)
         next = atomicAdd(ctr, 1u);
-    for (;;) {
-        const int64_t d = q + (int64_t)kQueues * __builtin_amdgcn_readfirstlane(next);
-        if (d >= n_dyn)
-            break;
+    int64_t i = __builtin_amdgcn_readfirstlane(next);
+    while (i < n_qh) {
+        if (lane == 0)
+            next = atomicAdd(ctr, 1u);
+        do_hub<S>(a, ws, lane, g, j, hub_base + 8 * i, n_hub, src, ysrc, row_bytes);
+        i = __builtin_amdgcn_readfirstlane(next);
+    }
+    // then queue q hands out items q, q + kQueues, ... of the rest
+    int64_t d = q + (int64_t)kQueues * (i - n_qh);
+    while (d < n_dyn) {
         if (lane == 0)
             next = atomicAdd(ctr, 1u);
         do_item<S>(a, ps, ws, lane, g, j, d, n_ch, n_med, n_long, src, ysrc, row_bytes);
+        d = q + (int64_t)kQueues * ((int64_t)__builtin_amdgcn_readfirstlane(next) - n_qh);
     }
 }
 

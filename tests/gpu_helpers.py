@@ -73,3 +73,26 @@ def assert_parity(C, Cref, Sref, dtype, what=""):
                 f"bound {tol:g}*S + {ABS:g}; first at ({i},{n}): gpu={C[i, n]!r} "
                 f"ref={Cref[i, n]!r} S={Sref[i, n]!r}")
     return float((err / np.maximum(Sref, 1e-30)).max()) if err.size else 0.0
+
+
+def compare_plan(p, tuning=None):
+    """The plan of problem p as the product call resolves it (its K, N and
+    tuning) exported from the device, against the plan oracle: bit-exact
+    lists, chunks, hub rows and hub chunks (the columns of p's rows ascend).
+    Returns the device plan."""
+    dt = sdl.DTYPE_F32 if p.dtype == "f32" else sdl.DTYPE_BF16
+    t = sdl.resolve_tuning(dt, p.N, tuning, K=p.K)
+    got = sdl.plan_export(torch.from_numpy(p.rowptr).cuda(), t,
+                          colind=torch.from_numpy(p.colind).cuda(), K=p.K)
+    want = oracle.plan_ref(p.rowptr, t.short_max, t.medium_max, t.chunk_nnz,
+                           hub_min=t.hub_min, slab_rows=t.slab_rows, K=p.K,
+                           colind=p.colind)
+    for k in ("n_short", "n_medium", "n_long", "n_chunks", "n_hub"):
+        assert got[k] == want[k], k
+    assert got["n_hub_chunks"] == want["hub_chunks"].shape[0]
+    assert np.array_equal(got["medium_rows"], want["medium_rows"])
+    assert np.array_equal(got["long_rows"], want["long_rows"])
+    assert np.array_equal(got["chunks"], want["chunks"])
+    assert np.array_equal(got["hub_rows"], want["hub_rows"])
+    assert np.array_equal(got["hub_chunks"], want["hub_chunks"])
+    return got

@@ -107,17 +107,43 @@ def test_host_validation_bf16_alignment():
 
 
 def test_tuned_rejects_bad_tuning():
-    bad = _binding._TuningStruct(10, 5, 4, 0)
+    T = _binding._TuningStruct
+    bad = T(short_max=10, medium_max=5, chunk_nnz=4, hub_min=-1, slab_rows=0)
     rc = raw_call("spmm_csr_tuned", 0, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 4,
                   ctypes.byref(bad), None)
     assert rc == 1
-    reserved = _binding._TuningStruct(1, 5, 4, 1)
+    reserved = T(short_max=1, medium_max=5, chunk_nnz=4, hub_min=-1, slab_rows=0,
+                 reserved=1)
     rc = raw_call("spmm_csr_tuned", 0, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 4,
                   ctypes.byref(reserved), None)
     assert rc == 1
     rc = raw_call("spmm_csr_tuned", 5, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 4,
                   None, None)
     assert rc == 1
+
+
+@pytest.mark.parametrize("dtype,K,N,hubs", [
+    (1, 1048576, 512, True),    # B 1 GiB: hub rows by default
+    (0, 1048576, 64, True),     # B exactly 256 MiB
+    (0, 262144, 64, False),     # B 64 MiB: the Infinity Cache holds it
+    (0, 4096, 256, False),      # B 4 MiB
+    (0, 1024, 32, False),
+    (0, 0, 64, False),
+])
+def test_resolve_hub_defaults(dtype, K, N, hubs):
+    """Hub rows by default only for a B of at least 256 MiB; slabs of 2 MiB of
+    B's rows; the hub threshold at least medium_max and 32 entries per slab."""
+    t = sdl.resolve_tuning(dtype, N, K=K)
+    esz = 2 if dtype == 1 else 4
+    assert t.slab_rows == max(1, (2 << 20) // (N * esz))
+    if hubs:
+        n_slabs = -(-K // t.slab_rows)
+        assert t.hub_min == max(t.medium_max, 32 * n_slabs)
+    else:
+        assert t.hub_min == 2 ** 31 - 1
+    # explicit values win
+    u = sdl.resolve_tuning(dtype, N, sdl.Tuning(hub_min=5, slab_rows=9), K=K)
+    assert (u.hub_min, u.slab_rows) == (5, 9)
 
 
 def test_noalloc_rejects_on_the_host():
@@ -151,15 +177,20 @@ def test_valid_call_without_gpu_reports_hip_error():
 
 
 def test_plan_export_validation():
-    counts = (ctypes.c_int64 * 4)()
-    t = _binding._TuningStruct(-1, 5, 4, 0)   # not resolved
-    rc = raw_call("spmm_plan_export", FAKE, 4, ctypes.byref(t), None, 0, counts,
-                  None, None, None)
-    assert rc == 1
-    t = _binding._TuningStruct(1, 5, 4, 0)
-    rc = raw_call("spmm_plan_export", FAKE, 0, ctypes.byref(t), None, 0, counts,
-                  None, None, None)
-    assert rc == 0 and list(counts) == [0, 0, 0, 0]
+    counts = (ctypes.c_int64 * 6)()
+    T = _binding._TuningStruct
+    t = T(short_max=-1, medium_max=5, chunk_nnz=4, hub_min=2 ** 31 - 1, slab_rows=1)
+    rc = raw_call("spmm_plan_export", FAKE, FAKE, 4, 4, ctypes.byref(t), None, 0, counts,
+                  None, None, None, None, None)
+    assert rc == 1                      # not resolved
+    t = T(short_max=1, medium_max=5, chunk_nnz=4, hub_min=10, slab_rows=1)
+    rc = raw_call("spmm_plan_export", FAKE, None, 4, 4, ctypes.byref(t), None, 0, counts,
+                  None, None, None, None, None)
+    assert rc == 1                      # hub rows possible: colind needed
+    t = T(short_max=1, medium_max=5, chunk_nnz=4, hub_min=2 ** 31 - 1, slab_rows=1)
+    rc = raw_call("spmm_plan_export", FAKE, None, 0, 4, ctypes.byref(t), None, 0, counts,
+                  None, None, None, None, None)
+    assert rc == 0 and list(counts) == [0] * 6
 
 
 def test_timing_read_empty():

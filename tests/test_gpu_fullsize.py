@@ -12,10 +12,8 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
-import sparse_dense_linear_amd as sdl
 import workloads as W
-from gpu_helpers import assert_parity, reference, run_gpu
+from gpu_helpers import assert_parity, compare_plan, reference, run_gpu
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -52,18 +50,10 @@ def test_full_streamed(name):
     p = W.make(name)
     log(f"{name}: generated nnz={p.nnz} in {time.time() - t:.1f}s")
 
-    dt = 0 if p.dtype == "f32" else 1
-    tun = sdl.resolve_tuning(dt, p.N)
-    got = sdl.plan_export(torch.from_numpy(p.rowptr).cuda(), tun)
-    want = oracle.plan_ref(p.rowptr, tun.short_max, tun.medium_max, tun.chunk_nnz)
-    for k in ("n_short", "n_medium", "n_long", "n_chunks"):
-        assert got[k] == want[k], k
-    assert np.array_equal(got["medium_rows"], want["medium_rows"])
-    assert np.array_equal(got["long_rows"], want["long_rows"])
-    assert np.array_equal(got["chunks"], want["chunks"])
+    got = compare_plan(p)
     log(f"{name}: plan equal ({got['n_medium']} medium, {got['n_long']} long, "
-        f"{got['n_chunks']} chunks)")
-    del got, want
+        f"{got['n_chunks']} chunks, {got['n_hub']} hubs, {got['n_hub_chunks']} hub chunks)")
+    del got
 
     C = run_gpu(p, fill=float("nan"))
     rows_per_block = max(1, BLOCK_ELEMS // p.N)

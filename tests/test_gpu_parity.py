@@ -15,7 +15,7 @@ import torch
 import oracle
 import sparse_dense_linear_amd as sdl
 import workloads as W
-from gpu_helpers import assert_parity, call, dev_arrays, reference, run_gpu
+from gpu_helpers import assert_parity, call, compare_plan, dev_arrays, reference, run_gpu
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -302,29 +302,34 @@ def test_plan_bit_exact_many_blocks(M, base, tuning):
 
 @pytest.mark.parametrize("name,make,tuning", PLAN_CASES, ids=[c[0] for c in PLAN_CASES])
 def test_plan_bit_exact(name, make, tuning):
-    p = make()
-    dt = 0 if p.dtype == "f32" else 1
-    t = sdl.resolve_tuning(dt, p.N, tuning)
-    rowptr = torch.from_numpy(p.rowptr).cuda()
-    got = sdl.plan_export(rowptr, t)
-    want = oracle.plan_ref(p.rowptr, t.short_max, t.medium_max, t.chunk_nnz)
-    for k in ("n_short", "n_medium", "n_long", "n_chunks"):
-        assert got[k] == want[k], k
-    assert np.array_equal(got["medium_rows"], want["medium_rows"])
-    assert np.array_equal(got["long_rows"], want["long_rows"])
-    assert np.array_equal(got["chunks"], want["chunks"])
+    compare_plan(make(), tuning)
 
 
 def test_plan_bit_exact_offset_rowptr():
     """rowptr[0] != 0 and a chunk count beyond the chunk table."""
     p = W.rows_with_lengths([9000, 0, 12000, 3, 7000], K=20000, N=32, seed=3)
     rp = np.concatenate([[5], 5 + p.rowptr[1:]]).astype(np.int32)
-    t = sdl.Tuning(2, 8, 3)
+    t = sdl.Tuning(2, 8, 3, hub_min=2 ** 31 - 1, slab_rows=1)   # resolved, no hubs
     got = sdl.plan_export(torch.from_numpy(rp).cuda(), t)
     want = oracle.plan_ref(rp, 2, 8, 3)
     assert got["n_chunks"] == want["n_chunks"] > 4096 + 5
     assert np.array_equal(got["chunks"], want["chunks"])
     assert np.array_equal(got["long_rows"], want["long_rows"])
+
+
+def test_plan_bit_exact_offset_rowptr_hubs():
+    """rowptr[0] != 0 with a hub row between two long rows: hub chunk bounds
+    are absolute positions too."""
+    p = W.rows_with_lengths([9000, 0, 12000, 3, 7000], K=20000, N=32, seed=4)
+    rp = np.concatenate([[5], 5 + p.rowptr[1:]]).astype(np.int32)
+    ci = np.concatenate([np.zeros(5, np.int32), p.colind]).astype(np.int32)
+    t = sdl.Tuning(2, 8, 300, hub_min=10000, slab_rows=1000)
+    got = sdl.plan_export(torch.from_numpy(rp).cuda(), t, colind=torch.from_numpy(ci).cuda(),
+                          K=p.K)
+    want = oracle.plan_ref(rp, 2, 8, 300, hub_min=10000, slab_rows=1000, K=p.K, colind=ci)
+    assert got["n_hub"] == want["n_hub"] == 1 and got["n_long"] == 2
+    for k in ("long_rows", "chunks", "hub_rows", "hub_chunks"):
+        assert np.array_equal(got[k], want[k]), k
 
 
 # ------------------------------------------------- scaled-down workloads
