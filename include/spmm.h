@@ -343,7 +343,11 @@ spmm_status_t fusedmm_csr_bf16in_f32acc(const int32_t *rowptr,
  * waits for `stream`, returns in *faults the number of such items since the
  * stream's scratch was created or last queried, and resets it.  A non-zero
  * count means that the outputs of the calls since the last query are not
- * valid.  The count is 0 unless the plan workgroups were kept from running.
+ * valid.  The count is 0 unless the plan workgroups were kept from running
+ * for that long, which can only happen when other kernels running at the
+ * same time (calls on other streams, or other libraries) hold the GPU's
+ * slots; callers that run concurrent kernels and need a guarantee should
+ * check it (the smoke check and the tests do after every call).
  */
 spmm_status_t spmm_stream_faults(void *stream, int64_t *faults);
 

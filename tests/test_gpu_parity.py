@@ -359,3 +359,20 @@ def test_small_n_powerlaw(N):
     p = W.powerlaw_rows(M=32768, N=N, seed=40 + N)
     Cref, Sref = reference(p)
     assert_parity(run_gpu(p), Cref, Sref, "f32", f"N={N}")
+
+
+def test_small_job_many_rows():
+    """A call that gathers only a few MB but has many rows: workgroups past
+    the first 64 product workgroups leave at once, and the rest (with the
+    plan's) must still cover every short tile, medium row and chunk."""
+    rng = np.random.default_rng(51)
+    M = 300000
+    lens = np.zeros(M, dtype=np.int64)
+    busy = rng.choice(M, 3000, replace=False)
+    lens[busy] = rng.choice([1, 3, 17, 40, 100], size=busy.size)
+    lens[busy[:4]] = 900                       # long rows: chunks
+    p = W.rows_with_lengths(lens, K=1000, N=16, seed=52)
+    assert p.nnz * p.N * 4 < (16 << 20)
+    C = run_gpu(p)
+    Cref, Sref = reference(p)
+    assert_parity(C, Cref, Sref, "f32", "small job, many rows")
