@@ -168,7 +168,8 @@ spmm_status_t spmm_csr_tuned(int32_t dtype, const int32_t *rowptr,
  * time (a per-GPU lock), but calls that overlap on the device -- e.g. made
  * on two streams of one GPU without ordering between them -- race on the
  * array and give wrong results: order them on one stream or with events.
- * The fault count of these calls is not reported by spmm_stream_faults.
+ * The fault count of these calls is kept in the array and reported by
+ * spmm_stream_faults (on the stream the calls used).
  */
 spmm_status_t spmm_csr_tuned_noalloc(int32_t dtype, const int32_t *rowptr,
                                      const int32_t *colind, const void *vals,
@@ -341,15 +342,27 @@ spmm_status_t fusedmm_csr_bf16in_f32acc(const int32_t *rowptr,
  * them; each poll is bounded (about a second), and an item whose entry
  * never became visible is left undone and counted.  spmm_stream_faults
  * waits for `stream`, returns in *faults the number of such items since the
- * stream's scratch was created or last queried, and resets it.  A non-zero
- * count means that the outputs of the calls since the last query are not
- * valid.  The count is 0 unless the plan workgroups were kept from running
- * for that long, which can only happen when other kernels running at the
- * same time (calls on other streams, or other libraries) hold the GPU's
- * slots; callers that run concurrent kernels and need a guarantee should
- * check it (the smoke check and the tests do after every call).
+ * stream's scratch was created or last queried, plus those of the
+ * no-allocation calls on the current device since the last query (read in
+ * the order of `stream`), and resets both counts.  A non-zero count means
+ * that the outputs of the calls since the last query are not valid.  The
+ * count is 0 unless the plan workgroups were kept from running for that
+ * long, which can only happen when other kernels running at the same time
+ * (calls on other streams, or other libraries) hold the GPU's slots;
+ * callers that run concurrent kernels and need a guarantee should check it
+ * (the smoke check and the tests do after every call).
  */
 spmm_status_t spmm_stream_faults(void *stream, int64_t *faults);
+
+/*
+ * Test hook for the path above: the calls enqueued after it poll at most
+ * `polls` times for each plan entry (0: they give up at once, so every
+ * item that needs the plan is left undone and counted, while every kernel
+ * still runs to its end).  polls < 0 restores the default bound (about a
+ * second); polls above the default is SPMM_ERROR_INVALID_VALUE.  Process-
+ * wide; not for production use.
+ */
+spmm_status_t spmm_debug_set_wait_polls(int64_t polls);
 
 /*
  * Give back the scratch block and the work buffer the library keeps for

@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     DTYPE_F32,
     SpmmError,
     Tuning,
+    debug_set_wait_polls,
     fusedmm,
     fusedmm_csr_f32,
     fusedmm_csr_bf16in_f32acc,

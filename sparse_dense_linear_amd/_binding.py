@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
                                    ctypes.POINTER(ctypes.c_int64)]
     L.spmm_stream_faults.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]
     L.spmm_stream_release.argtypes = [ctypes.c_void_p]
+    L.spmm_debug_set_wait_polls.argtypes = [I64]
     L.sddmm_csr_f32.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
     L.sddmm_csr_bf16in_f32acc.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
     L.fusedmm_csr_f32.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
@@ -95,7 +96,8 @@ def lib() -> ctypes.CDLL:
     for name in ("spmm_csr_f32", "spmm_csr_bf16in_f32acc", "spmm_csr_tuned",
                  "spmm_csr_tuned_noalloc",
                  "spmm_resolve_tuning", "spmm_plan_export", "spmm_timing_enable",
-                 "spmm_timing_read", "spmm_stream_faults", "spmm_stream_release"):
+                 "spmm_timing_read", "spmm_stream_faults", "spmm_stream_release",
+                 "spmm_debug_set_wait_polls"):
         getattr(L, name).restype = I32
     _lib = L
     return L
@@ -440,6 +442,13 @@ def stream_faults(stream=None) -> int:
     _check(lib().spmm_stream_faults(_stream_handle(None, stream), ctypes.byref(n)),
            "spmm_stream_faults")
     return n.value
+
+
+def debug_set_wait_polls(polls: int) -> None:
+    """Test hook: calls enqueued afterwards poll at most `polls` times for
+    each plan entry (0: give up at once); a negative value restores the
+    default bound."""
+    _check(lib().spmm_debug_set_wait_polls(int(polls)), "spmm_debug_set_wait_polls")
 
 
 def stream_release(stream=None) -> None:

@@ -285,7 +285,7 @@ hipError_t fresh_block(int dev, hipStream_t stream, size_t size, bool zero, void
     if (ptr == nullptr)
         return hipErrorOutOfMemory;
     if (zero && (err = hipMemsetAsync(ptr, 0, size, stream)) != hipSuccess) {
-        hipFreeAsync(ptr, stream);
+        (void)hipFreeAsync(ptr, stream);  // the memset's error is the one to report
         return err;
     }
     *out = ptr;
@@ -311,8 +311,10 @@ hipError_t scratch_for(StreamState &ss, size_t need, void **out, uint32_t *epoch
     hipError_t err = fresh_block(ss.dev, ss.stream, size, true, &ptr);
     if (err != hipSuccess)
         return err;
+    // the old block goes back after the calls that use it; a failed free
+    // would only leak it, the new block is in place either way
     if (ss.scratch)
-        hipFreeAsync(ss.scratch, ss.stream);
+        (void)hipFreeAsync(ss.scratch, ss.stream);
     ss.scratch = ptr;
     ss.scratch_size = size;
     ss.epoch = 1;
@@ -339,7 +341,7 @@ hipError_t aux_for(StreamState &ss, size_t need, void **out)
     if (err != hipSuccess)
         return err;
     if (ss.aux)
-        hipFreeAsync(ss.aux, ss.stream);
+        (void)hipFreeAsync(ss.aux, ss.stream);  // as for the scratch block
     ss.aux = ptr;
     ss.aux_size = size;
     *out = ptr;
@@ -548,6 +550,7 @@ spmm_status_t run_with(int32_t dtype, const int32_t *rowptr,
     wa.plan = carve((char *)scratch, lay);
     wa.shape = plan_shape(M);
     wa.epoch = epoch;
+    wa.wait_polls = current_wait_polls();
     const WorkerConfig cfg = choose_worker(dtype, N, B, C);
     err = launch_worker(cfg, wa, stream, tc.work0, tc.work1);
     if (err != hipSuccess)
@@ -627,6 +630,7 @@ spmm_status_t run_noalloc(int32_t dtype, const int32_t *rowptr,
     wa.plan = carve(fs->ptr, lay);
     wa.shape = plan_shape(M);
     wa.epoch = ++fs->epoch;
+    wa.wait_polls = current_wait_polls();
     const WorkerConfig cfg = choose_worker(dtype, N, B, C);
     err = launch_worker(cfg, wa, stream, nullptr, nullptr);
     if (err != hipSuccess)
@@ -906,7 +910,33 @@ spmm_status_t run_eb(int32_t dtype, const int32_t *rowptr, const int32_t *colind
     return SPMM_SUCCESS;
 }
 
+// Bound of the product's waits for plan entries, read by every call as it
+// is enqueued (lowered only by spmm_debug_set_wait_polls).
+std::atomic<int32_t> g_wait_polls{kWaitPolls};
+
+// Reads the fault count kept at the start of a plan scratch block in the
+// order of `stream`, and clears it if it is not zero.
+hipError_t take_fault_count(char *block, hipStream_t stream, uint32_t *out)
+{
+    uint32_t *word = (uint32_t *)(block + scratch_layout(0).faults);
+    uint32_t v = 0;
+    hipError_t err;
+    if ((err = hipMemcpyAsync(&v, word, sizeof v, hipMemcpyDeviceToHost, stream)) != hipSuccess ||
+        (err = hipStreamSynchronize(stream)) != hipSuccess)
+        return err;
+    if (v != 0) {
+        const uint32_t zero = 0;
+        if ((err = hipMemcpyAsync(word, &zero, sizeof zero, hipMemcpyHostToDevice, stream)) != hipSuccess ||
+            (err = hipStreamSynchronize(stream)) != hipSuccess)
+            return err;
+    }
+    *out = v;
+    return hipSuccess;
+}
+
 }  // namespace
+
+int32_t sdl::current_wait_polls() { return g_wait_polls.load(std::memory_order_relaxed); }
 
 extern "C" {
 
@@ -1059,6 +1089,7 @@ spmm_status_t spmm_plan_export(const int32_t *rowptr, const int32_t *colind,
         wa.plan = carve(dev_mem, lay);
         wa.shape = plan_shape(M);
         wa.epoch = 1;
+        wa.wait_polls = current_wait_polls();
         wa.C = nullptr;  // plan only
         const WorkerConfig cfg = choose_worker(SPMM_DTYPE_F32, 1, nullptr, nullptr);
         int64_t dcounts[6];
@@ -1100,7 +1131,9 @@ spmm_status_t spmm_plan_export(const int32_t *rowptr, const int32_t *colind,
             break;
         }
     } while (0);
-    hipFree(dev_mem);
+    const hipError_t ferr = hipFree(dev_mem);
+    if (st == SPMM_SUCCESS && ferr != hipSuccess)
+        st = fail_hip(ferr, "hipFree");
     return st;
 }
 
@@ -1201,25 +1234,38 @@ spmm_status_t spmm_stream_faults(void *stream_ptr, int64_t *faults)
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess)
         return fail_hip(err, "hipGetDevice");
-    StreamState *ss = stream_state(dev, stream, false);
-    if (ss == nullptr)
-        return SPMM_SUCCESS;  // no call on this stream yet
-    std::lock_guard<std::mutex> guard(ss->mu);
-    void *block = ss->scratch;
-    if (block == nullptr)
-        return SPMM_SUCCESS;  // no block (yet, or released)
-    uint32_t *word = (uint32_t *)((char *)block + scratch_layout(0).faults);
+    int64_t total = 0;
     uint32_t v = 0;
-    if ((err = hipMemcpyAsync(&v, word, sizeof v, hipMemcpyDeviceToHost, stream)) != hipSuccess ||
-        (err = hipStreamSynchronize(stream)) != hipSuccess)
-        return fail_hip(err, "reading the fault count");
-    if (v != 0) {
-        const uint32_t zero = 0;
-        if ((err = hipMemcpyAsync(word, &zero, sizeof zero, hipMemcpyHostToDevice, stream)) != hipSuccess ||
-            (err = hipStreamSynchronize(stream)) != hipSuccess)
-            return fail_hip(err, "clearing the fault count");
+    StreamState *ss = stream_state(dev, stream, false);
+    if (ss != nullptr) {
+        std::lock_guard<std::mutex> guard(ss->mu);
+        if (ss->scratch != nullptr) {  // else no block (yet, or released)
+            if ((err = take_fault_count((char *)ss->scratch, stream, &v)) != hipSuccess)
+                return fail_hip(err, "reading the fault count");
+            total += v;
+        }
     }
-    *faults = v;
+    // the no-allocation calls' count, in this device's fixed array
+    if (dev >= 0 && dev < kMaxDevices) {
+        FixedScratch &fs = g_fixed[dev];
+        std::lock_guard<std::mutex> guard(fs.mu);
+        if (fs.ptr != nullptr) {
+            if ((err = take_fault_count(fs.ptr, stream, &v)) != hipSuccess)
+                return fail_hip(err, "reading the fixed array's fault count");
+            total += v;
+        }
+    }
+    *faults = total;
+    return SPMM_SUCCESS;
+}
+
+spmm_status_t spmm_debug_set_wait_polls(int64_t polls)
+{
+    g_last_error.clear();
+    if (polls > kWaitPolls)
+        return fail(SPMM_ERROR_INVALID_VALUE,
+                    "polls above the default bound " + std::to_string(kWaitPolls));
+    g_wait_polls.store(polls < 0 ? kWaitPolls : (int32_t)polls, std::memory_order_relaxed);
     return SPMM_SUCCESS;
 }
 

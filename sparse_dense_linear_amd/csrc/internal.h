@@ -17,7 +17,10 @@ constexpr int kPlanBlockWaves = kWavesPerBlock;  // plan tiles per plan workgrou
 constexpr int kPlanMaxBlocks = kPlanMaxTiles / kPlanBlockWaves;
 constexpr int kPlanPrefixLoads = kPlanMaxBlocks / kWave;  // earlier blocks per lane
 static_assert(kPlanMaxBlocks % kWave == 0, "plan blocks are read a wavefront at a time");
-constexpr int64_t kChunkTableSlack = 4096;  // chunk table holds M + this
+constexpr int64_t kChunkTableSlack = 4096;
+// Polls of a product wavefront for a plan entry before it gives up on the
+// item (about a second); spmm_debug_set_wait_polls lowers it for tests.
+constexpr int32_t kWaitPolls = 1 << 19;  // chunk table holds M + this
 // Work queues of the product: kQueues grab counters per call, kQueueStride
 // 32-bit words apart (256 bytes, so they sit in different memory channels).
 constexpr int kQueues = 64;
@@ -123,7 +126,11 @@ struct WorkerArgs {
     PlanBuffers plan;
     PlanShape shape;
     uint32_t epoch;
+    int32_t wait_polls;    // bound of every wait for a plan entry
 };
+
+// The bound the next calls put in WorkerArgs::wait_polls.
+int32_t current_wait_polls();
 
 // Enqueue a call: one launch that plans and computes the product (the plan
 // alone when a.C is null).  start/stop (each may be null) are attached to

@@ -391,17 +391,15 @@ __device__ inline bool hub_ready(const WorkerArgs &a, int64_t l, int64_t *row)
     return true;
 }
 
-// Polls for a plan word.  The plan blocks are the first workgroups of the
-// launch, each XCD starts its workgroups in order, and a plan block never
-// waits, so the plan is running (and finishes) whenever a product
-// wavefront runs; the bound (about a second) only guarantees that every
-// wavefront exits.
-constexpr int kWaitPolls = 1 << 19;
-
+// Polls for a plan word, at most `polls` times.  The plan blocks are the
+// first workgroups of the launch, each XCD starts its workgroups in order,
+// and a plan block never waits, so the plan is running (and finishes)
+// whenever a product wavefront runs; the bound (kWaitPolls, about a
+// second) only guarantees that every wavefront exits.
 template <class Ready>
-__device__ inline bool wait_for(Ready ready)
+__device__ inline bool wait_for(int32_t polls, Ready ready)
 {
-    for (int i = 0; i < kWaitPolls; ++i) {
+    for (int32_t i = 0; i < polls; ++i) {
         if (ready())
             return true;
         __builtin_amdgcn_s_sleep(1);
@@ -447,7 +445,7 @@ __device__ inline void do_item(const WorkerArgs &a, const ProductShape &ps,
         // The row was cleared (device-coherent stores, completed) before its
         // chunk was published; the atomic adds address it through the
         // published row, so they come after the clearing.
-        if (wait_for([&]() { return chunk_ready(a, d, n_long, &row, &p0, &p1); }))
+        if (wait_for(a.wait_polls, [&]() { return chunk_ready(a, d, n_long, &row, &p0, &p1); }))
             do_range<S, true>(a, ws, lane, g, j, row, p0, p1, src, ysrc, row_bytes);
         else
             note_fault(a, lane);
@@ -457,7 +455,7 @@ __device__ inline void do_item(const WorkerArgs &a, const ProductShape &ps,
         const int64_t e = d - n_ch;
         const int64_t m = S::FUSED ? e : e - ps.n_dyn_tiles;
         if (m >= 0 && m < n_med) {
-            if (wait_for([&]() { return medium_ready(a, m, &row); }))
+            if (wait_for(a.wait_polls, [&]() { return medium_ready(a, m, &row); }))
                 do_range<S, false>(a, ws, lane, g, j, row, a.rowptr[row],
                                    a.rowptr[row + 1], src, ysrc, row_bytes);
             else
@@ -484,7 +482,7 @@ __device__ inline void do_hub(const WorkerArgs &a, WaveStage &ws, int lane,
 {
     const int64_t s = c / n_hub, l = c - s * n_hub;
     int64_t row = 0;
-    if (!wait_for([&]() { return hub_ready(a, l, &row); })) {
+    if (!wait_for(a.wait_polls, [&]() { return hub_ready(a, l, &row); })) {
         note_fault(a, lane);
         return;
     }
@@ -599,7 +597,7 @@ void call_kernel(WorkerArgs a, ProductShape ps)
     }
 
     int64_t n_med = 0, n_long = 0, n_ch = 0, n_hub = 0;
-    if (!wait_for([&]() { return counts_ready(a, &n_med, &n_long, &n_ch, &n_hub); })) {
+    if (!wait_for(a.wait_polls, [&]() { return counts_ready(a, &n_med, &n_long, &n_ch, &n_hub); })) {
         note_fault(a, lane);
         n_med = n_long = n_ch = n_hub = 0;
     }

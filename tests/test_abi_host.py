@@ -30,6 +30,7 @@ def test_header_declares_entry_points():
                  "spmm_resolve_tuning", "spmm_plan_export", "spmm_status_string",
                  "spmm_last_error", "spmm_timing_enable", "spmm_timing_read",
                  "spmm_stream_faults", "spmm_stream_release", "spmm_csr_tuned_noalloc",
+                 "spmm_debug_set_wait_polls",
                  "sddmm_csr_f32", "sddmm_csr_bf16in_f32acc",
                  "fusedmm_csr_f32", "fusedmm_csr_bf16in_f32acc"):
         assert must in names
@@ -160,6 +161,17 @@ def test_noalloc_rejects_on_the_host():
     rc = raw_call("spmm_csr_tuned_noalloc", 0, None, None, None, None, None, 0, 4, 4,
                   None, None)
     assert rc == 0                      # M == 0: nothing to do
+
+
+def test_wait_bound_hook_range():
+    """The wait-bound test hook takes 0 .. the default, or a negative value
+    for the default, and refuses a larger bound (host only, no HIP call)."""
+    L = sdl.lib()
+    assert L.spmm_debug_set_wait_polls(1 << 20) == 1
+    assert b"default" in L.spmm_last_error()
+    assert L.spmm_debug_set_wait_polls(0) == 0
+    assert L.spmm_debug_set_wait_polls(1 << 19) == 0
+    assert L.spmm_debug_set_wait_polls(-1) == 0
 
 
 def test_forced_allocation_failure(monkeypatch):
