@@ -133,7 +133,7 @@ def cpu_baseline(p, budget_s: float = 10.0, op: str = "spmm", dense=None) -> dic
                 oracle.fusedmm_ref(p.rowptr, p.colind, dense, p.B, p.B, p.N)
             reps += 1
             el = time.perf_counter() - t0
-            if el >= budget_s or reps >= 1000:
+            if el >= budget_s or reps >= 1_000_000:
                 return reps, el
 
     op_flops = flops(p) * (2 if op == "fusedmm" else 1)
