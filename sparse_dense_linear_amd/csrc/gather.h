@@ -143,12 +143,11 @@ template <> __device__ inline float load_val<SPMM_DTYPE_BF16>(const void *vals, 
 
 // Compile-time shape of one worker variant.  FUSED: the FusedMM variant,
 // whose entry values are computed on the fly (two gathers per entry, so
-// half as many entries in flight).  DEEP: the planned product may keep 16
-// gathers in flight per lane when one 64-lane group takes a whole fp32 row
-// of B, at 3 wavefronts per SIMD instead of 4 (measured 6 % faster on the
-// pruned workload; 32-lane groups, bf16 rows and FusedMM measured slower).
-template <int DT_, int VEC_, int G_, int NV_, bool BUF_, bool FUSED_ = false,
-          bool DEEP_ = false>
+// half as many entries in flight).  Every variant runs at 4 wavefronts per
+// SIMD: 16 gathers in flight per lane for whole fp32 rows of 256 columns at
+// 3 wavefronts per SIMD measured 5-11 % slower than 8 at 4 (pruned 4096^2,
+// N = 192 and 256), once queues stopped reserving items ahead.
+template <int DT_, int VEC_, int G_, int NV_, bool BUF_, bool FUSED_ = false>
 struct Shape {
     static constexpr bool BUF = BUF_;   // B addressed through a buffer resource
     static constexpr bool FUSED = FUSED_;
@@ -158,11 +157,9 @@ struct Shape {
     static constexpr int NV = NV_;
     static constexpr int R = kWave / G_;          // groups per wavefront
     static constexpr int COLS = G_ * VEC_ * NV_;  // columns per column pass
-    static constexpr bool WIDE = DEEP_ && !FUSED_ && G_ == kWave && NV_ == 1 &&
-                                 DT_ == SPMM_DTYPE_F32;
-    static constexpr int U0 = WIDE ? 16 : (NV_ == 1 ? 8 : (NV_ == 2 ? 4 : 2));
+    static constexpr int U0 = NV_ == 1 ? 8 : (NV_ == 2 ? 4 : 2);
     static constexpr int U = FUSED_ ? (U0 / 2 > 1 ? U0 / 2 : 1) : U0;  // entries in flight
-    static constexpr int MIN_WAVES = WIDE ? 3 : 4;   // wavefronts per SIMD
+    static constexpr int MIN_WAVES = 4;   // wavefronts per SIMD
     static constexpr int ESZ = ElemSize<DT_>::v;
 };
 

@@ -735,7 +735,7 @@ hipError_t launch_vec(int group, int nv, const WorkerArgs &a, hipStream_t s,
     case 16: return launch_shape<Shape<DT, VEC, 16, 1, BUF, FUSED>>(a, s, e0, e1);
     case 32: return launch_shape<Shape<DT, VEC, 32, 1, BUF, FUSED>>(a, s, e0, e1);
     case 64:
-        if (nv == 1) return launch_shape<Shape<DT, VEC, 64, 1, BUF, FUSED, true>>(a, s, e0, e1);
+        if (nv == 1) return launch_shape<Shape<DT, VEC, 64, 1, BUF, FUSED>>(a, s, e0, e1);
         if (nv == 2) return launch_shape<Shape<DT, VEC, 64, 2, BUF, FUSED>>(a, s, e0, e1);
         return launch_shape<Shape<DT, VEC, 64, 4, BUF, FUSED>>(a, s, e0, e1);
     default: return hipErrorInvalidValue;
