@@ -58,14 +58,21 @@ def run_fused(rowptr, colind, C, B, D, M, K, N, fill=float("nan"), shift=0):
     return E.cpu().numpy().reshape(M, N)
 
 
-def check(rowptr, colind, C, B, D, M, K, N, what="", shift=0):
+def check(rowptr, colind, C, B, D, M, K, N, what="", shift=0, margin=None):
+    """E against the oracle within the bar; with `margin`, also the worst
+    |E - Eref| / T over elements with T > 0 below margin * tol(N)."""
     E = run_fused(rowptr, colind, C, B, D, M, K, N, shift=shift)
     Eref, T = oracle.fusedmm_ref(rowptr, colind, C, B, D, N)
-    bad = ~(np.abs(E.astype(np.float64) - Eref) <= tol(N) * T + 1e-6)
+    err = np.abs(E.astype(np.float64) - Eref)
+    bad = ~(err <= tol(N) * T + 1e-6)
     if bad.any():
         i, n = np.argwhere(bad)[0]
         raise AssertionError(f"{what}: {int(bad.sum())} of {E.size} outside the bound; "
                              f"first ({i},{n}): gpu={E[i, n]!r} ref={Eref[i, n]!r} T={T[i, n]!r}")
+    if margin is not None:
+        live = T > 0
+        worst = float((err[live] / T[live]).max()) if live.any() else 0.0
+        assert worst <= margin * tol(N), f"{what}: worst err/T {worst:.3e}"
     return E
 
 
@@ -167,7 +174,9 @@ def test_powerlaw_pattern():
     rng = np.random.default_rng(6)
     C = rng.standard_normal((p.M, p.N)).astype(np.float32)
     D = rng.standard_normal((p.K, p.N)).astype(np.float32)
-    check(p.rowptr, p.colind, C, p.B.reshape(p.K, p.N), D, p.M, p.K, p.N, "powerlaw")
+    # measured worst err/T: 1.1e-7 against the bar's 2e-5
+    check(p.rowptr, p.colind, C, p.B.reshape(p.K, p.N), D, p.M, p.K, p.N, "powerlaw",
+          margin=0.05)
 
 
 # ---- bf16 inputs (one launch only) -------------------------------------

@@ -57,14 +57,21 @@ def run_sddmm(rowptr, colind, C, B, M, K, N, fill=float("nan")):
     return A.cpu().numpy()
 
 
-def check(rowptr, colind, C, B, M, K, N, what=""):
+def check(rowptr, colind, C, B, M, K, N, what="", margin=None):
+    """A against the oracle within the bar; with `margin`, also the worst
+    |A - Aref| / S over entries with S > 0 below margin * tol(N)."""
     A = run_sddmm(rowptr, colind, C, B, M, K, N)
     Aref, S = oracle.sddmm_ref(rowptr, colind, C, B, N)
-    bad = ~(np.abs(A.astype(np.float64) - Aref) <= tol(N) * S + 1e-6)
+    err = np.abs(A.astype(np.float64) - Aref)
+    bad = ~(err <= tol(N) * S + 1e-6)
     if bad.any():
         p = int(np.argmax(bad))
         raise AssertionError(f"{what}: {int(bad.sum())} of {A.size} outside the bound; "
                              f"first p={p}: gpu={A[p]!r} ref={Aref[p]!r} S={S[p]!r}")
+    if margin is not None:
+        live = S > 0
+        worst = float((err[live] / S[live]).max()) if live.any() else 0.0
+        assert worst <= margin * tol(N), f"{what}: worst err/S {worst:.3e}"
     return A
 
 
@@ -182,7 +189,9 @@ def test_workload_patterns(name, N):
     p = W.make(name)
     rng = np.random.default_rng(10)
     C = _dense(rng, p.M, N, p.dtype)
-    check(p.rowptr, p.colind, C, p.B.reshape(p.K, p.N), p.M, p.K, N, name)
+    # measured worst err/S: 1e-7 or less, against the bar's 1e-5 (N = 64)
+    # and 3e-5 (N = 256)
+    check(p.rowptr, p.colind, C, p.B.reshape(p.K, p.N), p.M, p.K, N, name, margin=0.05)
 
 
 def test_banded_pattern_sampled():
