@@ -305,8 +305,9 @@ spmm_status_t sddmm_csr_bf16in_f32acc(const int32_t *rowptr,
  *   nnz = rowptr[M] - rowptr[0] (a precondition).
  * E is overwritten; rows with no stored entries become zero rows.
  *
- * One launch on `stream` when N is a multiple of 4 and at most 1024 and C,
- * B, D and E are 16-byte aligned: the product's kernel (same plan, same
+ * One launch on `stream` when N is a multiple of 4 and at most 1024, C, B,
+ * D and E are 16-byte aligned, and either N <= 64 or nnz >= 32 * M (rows
+ * of 32 entries or more on average): the product's kernel (same plan, same
  * per-stream scratch) forms each entry's value from C_i and B_j where the
  * value is used, and no value array is written.  Otherwise two launches:
  * the SDDMM values are written to a scratch array of nnz floats (kept per

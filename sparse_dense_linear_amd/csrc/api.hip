@@ -57,6 +57,12 @@ constexpr int64_t kHubMinBBytes = (int64_t)256 << 20;
 constexpr int64_t kSlabBytes = (int64_t)2 << 20;
 constexpr int64_t kHubEntriesPerSlab = 32;
 
+// fp32 FusedMM runs in one launch for N up to kFusedShortRowsMaxN, and for
+// wider rows only when rows hold at least kFusedLongRowMean entries on
+// average.
+constexpr int64_t kFusedShortRowsMaxN = 64;
+constexpr int64_t kFusedLongRowMean = 32;
+
 spmm_status_t resolve(int32_t dtype, int64_t K, int64_t N, const spmm_tuning_t *req,
                       spmm_tuning_t *out)
 {
@@ -738,10 +744,17 @@ spmm_status_t run_fusedmm(const int32_t *rowptr, const int32_t *colind,
         return fail(SPMM_ERROR_INVALID_VALUE, "operand not aligned to its element size");
     // One launch when the FusedMM form of the worker covers the shape (fp32
     // rows of at most one column pass, C and B aligned like D): each entry's
-    // value is formed where it is used and never stored.
+    // value is formed where it is used and never stored.  Beyond 64
+    // columns that form pays only for long rows (its gathers come in pairs,
+    // half as many entries in flight per lane): with a mean row of 4 entries
+    // (power-law pattern) two launches were 1.5-2.2 x faster for N = 96 to
+    // 1024 and one launch faster for N = 32 and 64; with 410 (pruned
+    // pattern) one launch was level up to N = 512 and 1.3-1.5 x faster at
+    // 768 and 1024.
     const WorkerConfig cfg = choose_worker(SPMM_DTYPE_F32, N, D, E);
-    if (nnz > 0 && fused_fits(cfg, N) && ((uintptr_t)C) % 16 == 0 &&
-        ((uintptr_t)B) % 16 == 0)
+    const bool long_rows = nnz >= kFusedLongRowMean * M;
+    if (nnz > 0 && fused_fits(cfg, N) && (N <= kFusedShortRowsMaxN || long_rows) &&
+        ((uintptr_t)C) % 16 == 0 && ((uintptr_t)B) % 16 == 0)
         return run_with(SPMM_DTYPE_F32, rowptr, colind, nullptr, D, E, M, K, N,
                         nullptr, stream_ptr, false, nullptr, nullptr, false, C, B);
     // Otherwise two launches: SDDMM into a value array, then the product,

@@ -5,8 +5,9 @@ Kernels on Intel Max Series GPU", the FusedMM operation (Fig. 6,
 Algorithm 3).
 
 Two routes: one launch that forms each value where it is used (fp32, N a
-multiple of 4 up to 1024, operands 16-byte aligned), and otherwise SDDMM
-into a value array followed by the product.  Both are checked here.
+multiple of 4 up to 1024, operands 16-byte aligned, and N <= 64 or a mean
+row of 32 entries or more), and otherwise SDDMM into a value array followed
+by the product.  Both are checked here.
 
 Bar: |E_gpu - E_ref| <= 2 tol(N) T + 1e-6 per element, with the bound
 T[i,n] = sum_p S_p |D_jn| and tol(N) = max(1e-5, N 2^-23): each SDDMM value
@@ -110,6 +111,21 @@ def test_edge_rows(N):
     lengths[:len(EDGE)] = EDGE
     rp, ci = pattern(lengths, K, seed=N)
     check(rp, ci, dense(rng, M, N), dense(rng, K, N), dense(rng, K, N), M, K, N, f"N={N}")
+
+
+@pytest.mark.parametrize("N", [68, 96, 256, 512, 1024])
+def test_wide_rows_of_few_entries(N):
+    """N above 64 with a mean row of fewer than 32 entries takes the
+    two-launch route (one launch pays only for long rows there); rows of
+    every length class, against the oracle."""
+    rng = np.random.default_rng(N + 300)
+    M, K = 400, 3000
+    lengths = rng.choice([0, 1, 2, 3, 9, 16, 17, 40], size=M)
+    lengths[:3] = [300, 700, 0]          # a medium and a long row
+    assert lengths.sum() < 32 * M
+    rp, ci = pattern(lengths, K, seed=N + 300)
+    check(rp, ci, dense(rng, M, N), dense(rng, K, N), dense(rng, K, N), M, K, N,
+          f"N={N} few entries")
 
 
 @pytest.mark.parametrize("N", [8, 64, 256])

@@ -24,9 +24,9 @@ N = 1024
 M = 2048
 
 
-def _problem(seed):
+def _problem(seed, lo=0, hi=40):
     rng = np.random.default_rng(seed)
-    lengths = rng.integers(0, 40, M)
+    lengths = rng.integers(lo, hi, M)
     lengths[:6] = [0, 1, 300, 700, 2000, 5]   # empty, short, medium and long rows
     rowptr = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     cols = []
@@ -68,8 +68,10 @@ def test_B_above_4GiB(kernel):
 
 def test_fusedmm_B_above_4GiB():
     """FusedMM's one-launch form through flat addresses: B (and D, the same
-    array here) above 4 GiB."""
-    rowptr, colind, _ = _problem(seed=13)
+    array here) above 4 GiB.  At N = 1024 the one launch is taken for rows
+    of 32 entries or more on average, so the rows here are that long."""
+    rowptr, colind, _ = _problem(seed=13, lo=30, hi=60)
+    assert colind.size >= 32 * M
     g = torch.Generator(device="cuda")
     g.manual_seed(14)
     B = torch.randn(K * N, generator=g, device="cuda")
