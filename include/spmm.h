@@ -342,11 +342,14 @@ spmm_status_t fusedmm_csr_bf16in_f32acc(const int32_t *rowptr,
  * entries they need while the plan workgroups of the same launch write
  * them; each poll is bounded (about a second), and an item whose entry
  * never became visible is left undone and counted.  spmm_stream_faults
- * waits for `stream`, returns in *faults the number of such items since the
- * stream's scratch was created or last queried, plus those of the
- * no-allocation calls on the current device since the last query (read in
- * the order of `stream`), and resets both counts.  A non-zero count means
- * that the outputs of the calls since the last query are not valid.  The
+ * waits for `stream` and returns in *faults the number of such items in the
+ * calls on `stream` since the last query, plus those of the no-allocation
+ * calls on the current device since the last query (read in the order of
+ * `stream`).  The device only adds to the counts (they carry over when the
+ * stream's scratch grows; spmm_stream_release starts a new one), so an item
+ * counted while a query runs is reported by the next query, not lost.  A
+ * non-zero count means that the outputs of the calls since the last query
+ * are not valid.  The
  * count is 0 unless the plan workgroups were kept from running for that
  * long, which can only happen when other kernels running at the same time
  * (calls on other streams, or other libraries) hold the GPU's slots;

@@ -257,6 +257,7 @@ struct StreamState {
     void *scratch = nullptr;    // plan scratch block (zeroed when created)
     size_t scratch_size = 0;
     uint32_t epoch = 0;         // last epoch used on the block
+    uint32_t faults_seen = 0;   // the block's fault count at the last query
     void *aux = nullptr;        // work buffer (FusedMM values, carry slots)
     size_t aux_size = 0;
 };
@@ -317,10 +318,20 @@ hipError_t scratch_for(StreamState &ss, size_t need, void **out, uint32_t *epoch
     hipError_t err = fresh_block(ss.dev, ss.stream, size, true, &ptr);
     if (err != hipSuccess)
         return err;
-    // the old block goes back after the calls that use it; a failed free
-    // would only leak it, the new block is in place either way
-    if (ss.scratch)
+    if (ss.scratch) {
+        // the fault count goes on in the new block (the count only grows;
+        // queries report what it gained since the last one)
+        const size_t f = (size_t)scratch_layout(0).faults;
+        err = hipMemcpyAsync((char *)ptr + f, (char *)ss.scratch + f, sizeof(uint32_t),
+                             hipMemcpyDeviceToDevice, ss.stream);
+        if (err != hipSuccess) {
+            (void)hipFreeAsync(ptr, ss.stream);
+            return err;
+        }
+        // the old block goes back after the calls that use it; a failed
+        // free would only leak it, the new block is in place either way
         (void)hipFreeAsync(ss.scratch, ss.stream);
+    }
     ss.scratch = ptr;
     ss.scratch_size = size;
     ss.epoch = 1;
@@ -377,6 +388,7 @@ struct FixedScratch {
     std::mutex mu;             // held from epoch choice to enqueue
     char *ptr = nullptr;       // device address of `scratch` on this device
     uint32_t epoch = 0;
+    uint32_t faults_seen = 0;  // the array's fault count at the last query
 };
 
 FixedScratch g_fixed[kMaxDevices];
@@ -619,6 +631,7 @@ spmm_status_t run_noalloc(int32_t dtype, const int32_t *rowptr,
         if ((err = hipGetLastError()) != hipSuccess)
             return fail_hip(err, "clearing the fixed scratch");
         fs->epoch = 0;
+        fs->faults_seen = 0;  // the fill cleared the count too
     }
     WorkerArgs wa;
     wa.rowptr = rowptr;
@@ -927,23 +940,20 @@ spmm_status_t run_eb(int32_t dtype, const int32_t *rowptr, const int32_t *colind
 // is enqueued (lowered only by spmm_debug_set_wait_polls).
 std::atomic<int32_t> g_wait_polls{kWaitPolls};
 
-// Reads the fault count kept at the start of a plan scratch block in the
-// order of `stream`, and clears it if it is not zero.
-hipError_t take_fault_count(char *block, hipStream_t stream, uint32_t *out)
+// Reads the fault count kept in a plan scratch block, in the order of
+// `stream`, and returns what it gained since the last query (*seen).  The
+// device only ever adds to the count, so nothing is written back and no
+// increment made during the read is lost.
+hipError_t take_fault_count(char *block, hipStream_t stream, uint32_t *seen, uint32_t *out)
 {
-    uint32_t *word = (uint32_t *)(block + scratch_layout(0).faults);
+    const uint32_t *word = (const uint32_t *)(block + scratch_layout(0).faults);
     uint32_t v = 0;
     hipError_t err;
     if ((err = hipMemcpyAsync(&v, word, sizeof v, hipMemcpyDeviceToHost, stream)) != hipSuccess ||
         (err = hipStreamSynchronize(stream)) != hipSuccess)
         return err;
-    if (v != 0) {
-        const uint32_t zero = 0;
-        if ((err = hipMemcpyAsync(word, &zero, sizeof zero, hipMemcpyHostToDevice, stream)) != hipSuccess ||
-            (err = hipStreamSynchronize(stream)) != hipSuccess)
-            return err;
-    }
-    *out = v;
+    *out = v - *seen;  // modulo 2^32
+    *seen = v;
     return hipSuccess;
 }
 
@@ -1227,6 +1237,7 @@ spmm_status_t spmm_stream_release(void *stream_ptr)
     ss->scratch = nullptr;
     ss->scratch_size = 0;
     ss->epoch = 0;
+    ss->faults_seen = 0;  // a new block starts its count at zero
     if (ss->aux && (err = hipFreeAsync(ss->aux, stream)) != hipSuccess)
         return fail_hip(err, "hipFreeAsync");
     ss->aux = nullptr;
@@ -1253,7 +1264,8 @@ spmm_status_t spmm_stream_faults(void *stream_ptr, int64_t *faults)
     if (ss != nullptr) {
         std::lock_guard<std::mutex> guard(ss->mu);
         if (ss->scratch != nullptr) {  // else no block (yet, or released)
-            if ((err = take_fault_count((char *)ss->scratch, stream, &v)) != hipSuccess)
+            if ((err = take_fault_count((char *)ss->scratch, stream, &ss->faults_seen, &v)) !=
+                hipSuccess)
                 return fail_hip(err, "reading the fault count");
             total += v;
         }
@@ -1263,7 +1275,7 @@ spmm_status_t spmm_stream_faults(void *stream_ptr, int64_t *faults)
         FixedScratch &fs = g_fixed[dev];
         std::lock_guard<std::mutex> guard(fs.mu);
         if (fs.ptr != nullptr) {
-            if ((err = take_fault_count(fs.ptr, stream, &v)) != hipSuccess)
+            if ((err = take_fault_count(fs.ptr, stream, &fs.faults_seen, &v)) != hipSuccess)
                 return fail_hip(err, "reading the fixed array's fault count");
             total += v;
         }

@@ -60,3 +60,30 @@ def test_waits_that_give_up_are_counted_then_calls_are_exact(entry):
         torch.cuda.synchronize()
         assert sdl.stream_faults() == 0
         assert_parity(C.cpu().numpy().reshape(p.M, p.N), Cref, Sref, "f32", entry)
+
+
+def test_fault_count_survives_scratch_growth():
+    """Items counted in a stream's scratch block are still reported after a
+    larger call has replaced the block (the count moves to the new one)."""
+    p = mixed_problem()
+    args = dev_arrays(p)
+    s = torch.cuda.Stream()
+    C = torch.full((p.M * p.N,), float("nan"), device="cuda")
+    with torch.cuda.stream(s):
+        sdl.stream_release(s)                  # a fresh, small block
+        try:
+            sdl.debug_set_wait_polls(0)
+            sdl.spmm_csr_tuned(sdl.DTYPE_F32, *args, C, p.M, p.K, p.N, TUNING, stream=s)
+        finally:
+            sdl.debug_set_wait_polls(-1)
+        # a call with 40 x the rows needs a larger block
+        big = W.rows_with_lengths(np.full(40 * p.M, 3), 100, 8, seed=62)
+        bargs = dev_arrays(big)
+        Cb = torch.full((big.M * big.N,), float("nan"), device="cuda")
+        sdl.spmm_csr_f32(*bargs, Cb, big.M, big.K, big.N, stream=s)
+    s.synchronize()
+    assert sdl.stream_faults(s) > 0
+    assert sdl.stream_faults(s) == 0
+    Cref, Sref = reference(big)
+    assert_parity(Cb.cpu().numpy().reshape(big.M, big.N), Cref, Sref, "f32", "after growth")
+    sdl.stream_release(s)
