@@ -302,7 +302,10 @@ spmm_status_t sddmm_csr_bf16in_f32acc(const int32_t *rowptr,
  *
  *   C  M x N, B and D  K x N, E  M x N; all float32, row-major, leading
  *   dimension exactly N (D has the N columns of C and B).
- *   nnz = rowptr[M] - rowptr[0] (a precondition).
+ *   nnz = rowptr[M] - rowptr[0] (a precondition; on the two-launch route
+ *   below, a smaller nnz makes the product refuse to run, on the device,
+ *   and count a fault for spmm_stream_faults instead of reading past the
+ *   value array).
  * E is overwritten; rows with no stored entries become zero rows.
  *
  * One launch on `stream` when N is a multiple of 4 and at most 1024, C, B,

@@ -502,7 +502,7 @@ spmm_status_t run_with(int32_t dtype, const int32_t *rowptr,
                        bool vals_relative = false,
                        const void *dot_rows = nullptr,
                        const void *dot_cols = nullptr,
-                       StreamState *held = nullptr)
+                       StreamState *held = nullptr, int64_t vals_count = 0)
 {
     spmm_status_t st = check_args(dtype, rowptr, B, C, M, K, N);
     if (st != SPMM_SUCCESS)
@@ -557,6 +557,7 @@ spmm_status_t run_with(int32_t dtype, const int32_t *rowptr,
     wa.colind = colind;
     wa.vals = vals;
     wa.vals_relative = vals_relative ? 1 : 0;
+    wa.vals_count = vals_count;
     wa.B = B;
     wa.C = C;
     wa.dot_rows = dot_rows;
@@ -638,6 +639,7 @@ spmm_status_t run_noalloc(int32_t dtype, const int32_t *rowptr,
     wa.colind = colind;
     wa.vals = vals;
     wa.vals_relative = 0;
+    wa.vals_count = 0;
     wa.B = B;
     wa.C = C;
     wa.dot_rows = nullptr;
@@ -819,7 +821,7 @@ spmm_status_t run_fusedmm(const int32_t *rowptr, const int32_t *colind,
     if (st == SPMM_SUCCESS)
         st = run_with(SPMM_DTYPE_F32, rowptr, colind, vals, D, E, M, K, N, nullptr,
                       stream_ptr, true, nnz > 0 ? nullptr : tc.work0, tc.work1,
-                      true, nullptr, nullptr, ss);
+                      true, nullptr, nullptr, ss, nnz);
     if (st == SPMM_SUCCESS && timing) {
         std::lock_guard<std::mutex> lock(g_time_mu);
         g_timed.push_back(tc);

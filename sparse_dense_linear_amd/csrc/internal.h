@@ -112,6 +112,7 @@ struct WorkerArgs {
     const int32_t *colind;
     const void *vals;      // value of entry p at vals[p] (or vals[p - rowptr[0]])
     int32_t vals_relative; // 1: vals is indexed from rowptr[0], not from 0
+    int64_t vals_count;    // vals_relative: entries in vals
     const void *B;         // FusedMM: D, the rows that the values weight
     float *C;              // null: plan only (no product)
     // FusedMM only (null otherwise): the value of an entry of row i at

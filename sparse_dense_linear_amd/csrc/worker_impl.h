@@ -565,6 +565,14 @@ void call_kernel(WorkerArgs a, ProductShape ps)
                               q * kQueueStride] = 0;
         __syncthreads();  // the block's LDS now serves the product
     }
+    // Values read from an array of vals_count entries (the SDDMM values of
+    // FusedMM's two-launch route): a pattern with more stored entries than
+    // that (an nnz below rowptr[M] - rowptr[0]) is refused before any value
+    // is read, and counted as a fault.
+    if (a.vals_relative && (int64_t)a.rowptr[a.M] - a.rowptr[0] > a.vals_count) {
+        note_fault(a, lane);
+        return;
+    }
 
     const int g = lane / S::G;
     const int j = lane % S::G;

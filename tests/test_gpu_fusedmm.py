@@ -128,6 +128,29 @@ def test_wide_rows_of_few_entries(N):
           f"N={N} few entries")
 
 
+def test_two_launch_route_refuses_a_short_nnz():
+    """nnz below rowptr[M] - rowptr[0] (a broken precondition) on the
+    two-launch route: the SDDMM writes only nnz values, and the product,
+    which would read the missing ones past the value array, is refused on
+    the device and counted as a fault; the next call with the right nnz is
+    exact."""
+    rng = np.random.default_rng(71)
+    M, K, N = 400, 3000, 128                   # N > 64, short rows: two launches
+    lengths = rng.choice([0, 1, 2, 3, 9, 16, 17, 40], size=M)
+    rp, ci = pattern(lengths, K, seed=71)
+    stored = int(rp[-1])
+    assert stored < 32 * M
+    C, B, D = dense(rng, M, N), dense(rng, K, N), dense(rng, K, N)
+    args = (torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda(), _dev(C), _dev(B),
+            _dev(D))
+    E = torch.full((M * N,), float("nan"), dtype=torch.float32, device="cuda")
+    assert sdl.stream_faults() == 0
+    sdl.fusedmm_csr_f32(*args, E, M, K, N, stored // 2)
+    torch.cuda.synchronize()
+    assert sdl.stream_faults() > 0
+    check(rp, ci, C, B, D, M, K, N, "right nnz after a short one")
+
+
 @pytest.mark.parametrize("N", [8, 64, 256])
 def test_unaligned_operands(N):
     """C and B one float past a 16-byte boundary take the two-launch route
