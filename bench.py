@@ -43,6 +43,18 @@ sys.path.insert(0, ROOT)
 METRIC = ("SpMM GFLOP/s (2·nnz·N) and effective HBM GB/s as % of peak, "
           "1 MI355X")
 HBM_PEAK_GBPS = 8000.0
+# Vector fp32 peak of the part: 256 CUs x 4 SIMDs x 16 lanes x 2 flops per
+# FMA x 2 (packed fp32) x 2.4 GHz = 157.3 TFLOP/s (78.6 without packed math,
+# which this build does not use).
+VECTOR_FP32_PEAK_TFLOPS = 157.3
+
+
+def roofline_bound(op_flops: float, op_bytes: float) -> str:
+    """'alu' when the work's arithmetic intensity (flops per algorithmic
+    byte) is above the part's balance point (vector fp32 peak over HBM
+    peak, 19.7 flops per byte), else 'hbm'."""
+    balance = VECTOR_FP32_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    return "alu" if op_flops / op_bytes > balance else "hbm"
 DEFAULT_WORKLOAD = "powerlaw_262k_n64"
 KERNEL_SOURCES = ["sparse_dense_linear_amd/csrc/worker.hip",
                   "sparse_dense_linear_amd/csrc/worker_impl.h",
@@ -365,6 +377,38 @@ def main() -> int:
     cold_best = min(cold) if cold else None
     cold_ach = None if not cold_med else mb / (cold_med * 1e-3) / 1e9
 
+    traffic = measured_traffic(p.name, args.op)
+    if roofline_bound(op_flops, mb) == "hbm":
+        roofline = {
+            "bound": "hbm",
+            "achieved": None if achieved is None else round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": None if achieved is None else round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            # the same launch after a 1 GiB eviction of L2 and the Infinity
+            # Cache (median of the cold calls below)
+            "cold_achieved": None if cold_ach is None else round(cold_ach, 2),
+            "cold_frac": None if cold_ach is None else round(cold_ach / HBM_PEAK_GBPS, 4),
+        }
+    else:
+        # arithmetic intensity above the balance point: the vector fp32 ALU
+        # roofline, flops per launch over the launch's duration
+        tf = None if worker_avg_ms <= 0 else op_flops / (worker_avg_ms * 1e-3) / 1e12
+        cold_tf = None if not cold_med else op_flops / (cold_med * 1e-3) / 1e12
+        roofline = {
+            "bound": "alu",
+            "achieved": None if tf is None else round(tf, 3),
+            "peak": VECTOR_FP32_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": None if tf is None else round(tf / VECTOR_FP32_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "cold_achieved": None if cold_tf is None else round(cold_tf, 3),
+            "cold_frac": None if cold_tf is None else round(cold_tf / VECTOR_FP32_PEAK_TFLOPS, 4),
+            "flops_per_byte": round(op_flops / mb, 2),
+            "hbm_achieved": None if achieved is None else round(achieved, 2),
+        }
+
     out = {
         "metric": METRIC if args.op in ("spmm", "eb") else METRIC.replace(
             "SpMM", {"sddmm": "SDDMM", "fusedmm": "FusedMM"}[args.op]).replace(
@@ -388,18 +432,7 @@ def main() -> int:
         "min_bytes": mb,
         "flops_per_step": op_flops,
         "kernel_ms": {"call": round(worker_avg_ms, 6)},
-        "roofline": {
-            "bound": "hbm",
-            "achieved": None if achieved is None else round(achieved, 2),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": None if achieved is None else round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(p.name, args.op),
-            # the same launch after a 1 GiB eviction of L2 and the Infinity
-            # Cache (median of the cold calls below)
-            "cold_achieved": None if cold_ach is None else round(cold_ach, 2),
-            "cold_frac": None if cold_ach is None else round(cold_ach / HBM_PEAK_GBPS, 4),
-        },
+        "roofline": roofline,
         "cold": {"median_ms": cold_med, "best_ms": cold_best,
                  "reps": len(cold),
                  "eff_GBps_median": None if not cold_med else round(mb / (cold_med * 1e-3) / 1e9, 2),

@@ -70,3 +70,18 @@ def test_source_hash_covers_every_kernel_source():
     files = {f"sparse_dense_linear_amd/csrc/{f}" for f in os.listdir(csrc)
              if f.endswith((".hip", ".h")) and f != "ceiling.hip"}
     assert files == set(bench.KERNEL_SOURCES)
+
+
+def test_roofline_bound_follows_arithmetic_intensity():
+    """Work above the balance point (157.3 TFLOP/s over 8 TB/s, 19.7 flops
+    per algorithmic byte) is measured against the vector ALU peak: the
+    pruned (about 39-52 flops per byte) and skewed (about 31) products, not
+    the uniform (2.6), power-law (1.0) or banded (6.4) ones."""
+    for name, expect in (("uniform_1k_n32", "hbm"), ("pruned_4k_n256_f32", "alu"),
+                         ("pruned_4k_n256_bf16", "alu")):
+        p = W.make(name)
+        assert bench.roofline_bound(bench.flops(p), bench.min_bytes(p)) == expect, name
+    # the skewed, banded and power-law intensities, from their sizes
+    assert bench.roofline_bound(123.0e9, 3.946e9) == "alu"
+    assert bench.roofline_bound(34.36e9, 5.385e9) == "hbm"
+    assert bench.roofline_bound(140.3e6, 144.0e6) == "hbm"
