@@ -151,6 +151,8 @@ SDL_DECLARE_LAUNCH(launch_bf16_buf)
 SDL_DECLARE_LAUNCH(launch_bf16_flat)
 SDL_DECLARE_LAUNCH(launch_fused_buf)
 SDL_DECLARE_LAUNCH(launch_fused_flat)
+SDL_DECLARE_LAUNCH(launch_f32_pair)
+SDL_DECLARE_LAUNCH(launch_bf16_pair)
 #undef SDL_DECLARE_LAUNCH
 
 // One SDDMM call (sddmm.hip): A[p - rowptr[0]] = <C_i, B_colind[p]>.

@@ -47,6 +47,9 @@ bool fused_fits(const WorkerConfig &cfg, int64_t N)
            N <= (int64_t)cfg.group * cfg.vec * cfg.nv;
 }
 
+// B of at least this size (more than the Infinity Cache) takes the PAIR form.
+constexpr uint64_t kPairMinBBytes = (uint64_t)256 << 20;
+
 hipError_t launch_call(const WorkerConfig &cfg, const WorkerArgs &a,
                        hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
@@ -60,6 +63,21 @@ hipError_t launch_call(const WorkerConfig &cfg, const WorkerArgs &a,
         if (!fused_fits(cfg, a.N) || a.dot_cols == nullptr)
             return hipErrorInvalidValue;
         return buf ? launch_fused_buf(cfg, a, s, e0, e1) : launch_fused_flat(cfg, a, s, e0, e1);
+    }
+    // B larger than the Infinity Cache, read through a buffer resource, with
+    // rows of 512 bytes (two column passes of 16 lanes): the PAIR form
+    // (medium rows two at a time, one column half per item).  Rows of 1 KB
+    // keep the one-pass form: the skewed bf16 workload (N = 512), whose
+    // hub chunks and short tiles would then take two column passes each,
+    // was 5 % slower in the PAIR form.
+    const int64_t half_vecs = cfg.vec > 0 ? a.N / 2 / cfg.vec : 0;
+    if (buf && b_bytes >= kPairMinBBytes && cfg.vec * esz == 16 && a.N % (2 * cfg.vec) == 0 &&
+        half_vecs == 16) {
+        WorkerConfig pc = cfg;
+        pc.group = (int)half_vecs;
+        pc.nv = 1;
+        return cfg.dtype == SPMM_DTYPE_F32 ? launch_f32_pair(pc, a, s, e0, e1)
+                                           : launch_bf16_pair(pc, a, s, e0, e1);
     }
     if (cfg.dtype == SPMM_DTYPE_F32)
         return buf ? launch_f32_buf(cfg, a, s, e0, e1) : launch_f32_flat(cfg, a, s, e0, e1);

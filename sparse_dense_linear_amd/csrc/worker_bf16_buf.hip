@@ -17,4 +17,10 @@ hipError_t launch_bf16_buf(const WorkerConfig &cfg, const WorkerArgs &a,
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_bf16_pair(const WorkerConfig &cfg, const WorkerArgs &a,
+                           hipStream_t s, hipEvent_t e0, hipEvent_t e1)
+{
+    return launch_pair<SPMM_DTYPE_BF16, 8, true>(cfg.group, a, s, e0, e1);
+}
+
 }  // namespace sdl

@@ -16,4 +16,10 @@ hipError_t launch_f32_buf(const WorkerConfig &cfg, const WorkerArgs &a,
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_f32_pair(const WorkerConfig &cfg, const WorkerArgs &a,
+                          hipStream_t s, hipEvent_t e0, hipEvent_t e1)
+{
+    return launch_pair<SPMM_DTYPE_F32, 4, true>(cfg.group, a, s, e0, e1);
+}
+
 }  // namespace sdl

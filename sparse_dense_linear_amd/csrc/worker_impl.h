@@ -162,6 +162,27 @@ __device__ inline bool medium_ready(const WorkerArgs &a, int64_t i, int64_t *row
     return true;
 }
 
+// Rows of medium entries 2u and 2u + 1 (the second -1 when 2u + 1 = n_med)
+// if both are published: both words are read by one load.  Never waits.
+__device__ inline bool medium_pair_ready(const WorkerArgs &a, int64_t u, int64_t n_med,
+                                         int lane, int64_t *ra, int64_t *rb)
+{
+    const int64_t m = 2 * u + (lane & 1);
+    const uint64_t w = m < n_med ? tag_load(a.plan.medium_rows + m) : 0;
+    const uint64_t wa = __shfl(w, 0), wb = __shfl(w, 1);
+    if (!tag_is(wa, a.epoch))
+        return false;
+    if (2 * u + 1 < n_med) {
+        if (!tag_is(wb, a.epoch))
+            return false;
+        *rb = (uint32_t)wb;
+    } else {
+        *rb = -1;
+    }
+    *ra = (uint32_t)wa;
+    return true;
+}
+
 // Add one column pass of a row's partial sums into C with device atomics.
 // After reduce_groups every group holds the sums; group 0 lays each of its
 // vectors out in the wavefront's LDS area in column order, and then all 64
@@ -391,6 +412,70 @@ __device__ inline bool hub_ready(const WorkerArgs &a, int64_t l, int64_t *row)
     return true;
 }
 
+// Two medium rows ra and rb (rb < 0: none) in one wavefront, over the
+// column pass starting at col0: lanes [0, 32) load ra's entries and lanes
+// [32, 64) rb's, groups [0, R/2) consume the first half of the lanes and the
+// others the second, and each half is reduced and stored on its own.  Both
+// rows are medium rows, so each holds at least one entry.
+template <class S>
+__device__ void do_pair(const WorkerArgs &a, int lane, int g, int j, int64_t ra,
+                        int64_t rb, int64_t col0, const BSrc &src, uint32_t row_bytes)
+{
+    static_assert(S::PAIR && S::R >= 2 && S::NV == 1 && !S::FUSED, "pair shapes only");
+    constexpr int H = kWave / 2;
+    const bool upper = lane >= H;
+    const int64_t row = upper ? rb : ra;
+    const bool has = row >= 0;
+    int64_t p0 = 0, p1 = 0;
+    if (has) {
+        p0 = a.rowptr[row];
+        p1 = a.rowptr[row + 1];
+    }
+    const int len = (int)(p1 - p0);
+    const int len_a = __shfl(len, 0), len_b = __shfl(len, H);
+    const int longest = len_a > len_b ? len_a : len_b;
+    const int n_chunks = (longest + H - 1) / H;
+    const int hl = lane & (H - 1);
+    // the group's row: the lower or the upper half of the lanes
+    const bool g_upper = g >= S::R / 2;
+    const int g_len = g_upper ? len_b : len_a;
+    const int g_first = g * S::G - (g_upper ? H : 0);  // within its half
+    const LaneCols<S> lc = lane_cols<S>(a.N, col0, j);
+    float acc[S::NV][S::VEC];
+    zero_acc<S>(acc);
+    // positions past a row read its last entry (valid address)
+    int32_t nc = 0;
+    float nvv = 0.0f;
+    if (has) {
+        const int64_t p = p0 + hl < p1 ? p0 + hl : p1 - 1;
+        nc = a.colind[p];
+        nvv = load_val<S::DT>(a.vals, p);
+    }
+    for (int c = 0; c < n_chunks; ++c) {
+        const int32_t col = nc;
+        const float val = nvv;
+        if (c + 1 < n_chunks && has) {
+            const int64_t p = p0 + (int64_t)(c + 1) * H + hl;
+            const int64_t q = p < p1 ? p : p1 - 1;
+            nc = a.colind[q];
+            nvv = load_val<S::DT>(a.vals, q);
+        }
+        int cnt = g_len - c * H - g_first;
+        cnt = cnt < 0 ? 0 : (cnt > S::G ? S::G : cnt);
+        consume_lanes<S>(col, val, g * S::G, cnt, src, row_bytes, lc, acc);
+    }
+    // each half's groups add up their partial rows
+#pragma unroll
+    for (int off = S::G; off < H; off <<= 1)
+#pragma unroll
+        for (int x = 0; x < S::VEC; ++x)
+            acc[0][x] += __shfl_xor(acc[0][x], off);
+    if (g == 0 && ra >= 0)
+        emit_row<S, false>(a.C, ra, a.N, col0, j, acc);
+    if (g == S::R / 2 && rb >= 0)
+        emit_row<S, false>(a.C, rb, a.N, col0, j, acc);
+}
+
 // Polls for a plan word, at most `polls` times.  The plan blocks are the
 // first workgroups of the launch, each XCD starts its workgroups in order,
 // and a plan block never waits, so the plan is running (and finishes)
@@ -617,7 +702,9 @@ void call_kernel(WorkerArgs a, ProductShape ps)
         note_fault(a, lane);
         n_med = n_long = n_ch = n_hub = 0;
     }
-    const int64_t n_dyn = n_ch + n_med + ps.n_dyn_tiles;
+    // PAIR form: medium rows leave the shared list for the pair items below
+    const int64_t n_med_list = S::PAIR ? 0 : n_med;
+    const int64_t n_dyn = n_ch + n_med_list + ps.n_dyn_tiles;
     // One item per grab: consecutive items go to different wavefronts at
     // about the same time, so the whole GPU sweeps the item list in order
     // (rows that share columns of B, as in banded matrices, are gathered
@@ -649,23 +736,54 @@ void call_kernel(WorkerArgs a, ProductShape ps)
         do_hub<S>(a, ws, lane, g, j, hub_base + 8 * i, n_hub, src, ysrc, row_bytes);
         i = __builtin_amdgcn_readfirstlane(next);
     }
+    // PAIR form: then the medium rows, two consecutive ones per item and
+    // one column half per item.  XCDs 0-3 take the first half of B's
+    // columns and XCDs 4-7 the second, each XCD a contiguous quarter of the
+    // pairs in row order (its 8 queues interleaved), so the rows of B that
+    // neighbouring rows gather (a band) are read from that XCD's L2 at half
+    // the width: a window of B rows twice as tall fits it.
+    int64_t n_qp = 0;
+    if constexpr (S::PAIR) {
+        const int64_t n_pairs = (n_med + 1) / 2;
+        const int64_t u_lo = (int64_t)(x & 3) * n_pairs / 4;
+        const int64_t u_hi = (int64_t)((x & 3) + 1) * n_pairs / 4;
+        n_qp = u_hi - u_lo > k ? (u_hi - u_lo - k + 7) / 8 : 0;
+        const int64_t col0 = (int64_t)(x >> 2) * S::COLS;
+        const bool pahead =
+            n_qp > kGrabAheadItems * ((int64_t)gridDim.x * kWavesPerBlock / kQueues);
+        while (i - n_qh < n_qp) {
+            const int64_t u = u_lo + k + 8 * (i - n_qh);
+            if (pahead && lane == 0)
+                next = atomicAdd(ctr, 1u);
+            int64_t ra = -1, rb = -1;
+            if (wait_for(a.wait_polls,
+                         [&]() { return medium_pair_ready(a, u, n_med, lane, &ra, &rb); }))
+                do_pair<S>(a, lane, g, j, ra, rb, col0, src, row_bytes);
+            else
+                note_fault(a, lane);
+            if (!pahead && lane == 0)
+                next = atomicAdd(ctr, 1u);
+            i = __builtin_amdgcn_readfirstlane(next);
+        }
+    }
     // then queue q hands out items q, q + kQueues, ... of the rest.  The
     // next grab is issued before the current item only when the queue holds
     // many items per wavefront (then its latency would recur item after
     // item); with few, a grab made early reserves an item that no idle
     // wavefront may take, and the first wavefronts to arrive take two items
     // each while later ones find the queue empty.
-    int64_t d = q + (int64_t)kQueues * (i - n_qh);
+    int64_t d = q + (int64_t)kQueues * (i - n_qh - n_qp);
     const int64_t n_q = n_dyn > q ? (n_dyn - q + kQueues - 1) / kQueues : 0;
     const bool ahead =
         n_q > kGrabAheadItems * ((int64_t)gridDim.x * kWavesPerBlock / kQueues);
     while (d < n_dyn) {
         if (ahead && lane == 0)
             next = atomicAdd(ctr, 1u);
-        do_item<S>(a, ps, ws, lane, g, j, d, n_ch, n_med, n_long, src, ysrc, row_bytes);
+        do_item<S>(a, ps, ws, lane, g, j, d, n_ch, n_med_list, n_long, src, ysrc, row_bytes);
         if (!ahead && lane == 0)
             next = atomicAdd(ctr, 1u);
-        d = q + (int64_t)kQueues * ((int64_t)__builtin_amdgcn_readfirstlane(next) - n_qh);
+        d = q + (int64_t)kQueues *
+                ((int64_t)__builtin_amdgcn_readfirstlane(next) - n_qh - n_qp);
     }
 }
 
@@ -729,6 +847,16 @@ hipError_t launch_shape(const WorkerArgs &a, hipStream_t stream,
     hipExtLaunchKernelGGL(call_kernel<S>, dim3((unsigned)blocks), dim3(kBlock),
                           0, stream, start, stop, 0, a, ps);
     return hipGetLastError();
+}
+
+// The PAIR form for rows of B two column passes of 16 lanes wide.
+template <int DT, int VEC, bool BUF>
+hipError_t launch_pair(int group, const WorkerArgs &a, hipStream_t s, hipEvent_t e0,
+                       hipEvent_t e1)
+{
+    if (group != 16)
+        return hipErrorInvalidValue;
+    return launch_shape<Shape<DT, VEC, 16, 1, BUF, false, true>>(a, s, e0, e1);
 }
 
 template <int DT, int VEC, bool BUF, bool FUSED = false>
