@@ -287,7 +287,7 @@ void eb_kernel(EbArgs a)
                 n = n < 0 ? 0 : (n > E::UE ? E::UE : n);
                 const int q = k0 < nb ? k0 : nb - 1;
                 Batch<S> bt;
-                issue<S>(bt, st, q, n > 0 ? n : 1, src, row_bytes, lc);
+                issue<S>(bt, st, q, n, src, row_bytes, lc);
                 float acc[S::NV][S::VEC], hacc[S::NV][S::VEC];
                 zero_acc<S>(acc);
                 zero_acc<S>(hacc);
@@ -457,7 +457,7 @@ hipError_t launch_eb(const WorkerConfig &cfg, const EbArgs &a, hipStream_t s,
 {
     const int esz = cfg.dtype == SPMM_DTYPE_BF16 ? 2 : 4;
     const uint64_t b_bytes = (uint64_t)a.K * (uint64_t)a.N * (uint64_t)esz;
-    if (b_bytes < 0xFFFFFFFFull)
+    if (b_bytes <= kBufMaxBytes)
         return launch_eb_dtype<true>(cfg, a, s, e0, e1);
     return launch_eb_dtype<false>(cfg, a, s, e0, e1);
 }

@@ -24,6 +24,12 @@ constexpr int32_t kWaitPolls = 1 << 19;  // chunk table holds M + this
 // Work queues of the product: kQueues grab counters per call, kQueueStride
 // 32-bit words apart (256 bytes, so they sit in different memory channels).
 constexpr int kQueues = 64;
+// B is read through a buffer resource (32-bit byte offsets, record count =
+// B's size in bytes) when it holds at most this many bytes; a gather slot
+// with no entry then loads from kNoRowOffset, past the record count, and
+// reads zeros.
+constexpr uint32_t kNoRowOffset = 0xFFFFFFF0u;
+constexpr uint64_t kBufMaxBytes = kNoRowOffset;
 constexpr int kQueueStride = 64;
 // Entries of one short tile staged per wavefront; short_max is capped at
 // kShortCap / R (R = row groups per wavefront) so that a tile of at least R

@@ -57,7 +57,7 @@ hipError_t launch_call(const WorkerConfig &cfg, const WorkerArgs &a,
     // is below 4 GiB, otherwise through flat 64-bit addresses.
     const int esz = cfg.dtype == SPMM_DTYPE_BF16 ? 2 : 4;
     const uint64_t b_bytes = (uint64_t)a.K * (uint64_t)a.N * (uint64_t)esz;
-    const bool buf = b_bytes < 0xFFFFFFFFull;
+    const bool buf = b_bytes <= kBufMaxBytes;
     if (a.dot_rows != nullptr) {
         // FusedMM: 16-byte vectors, the whole row in one column pass.
         if (!fused_fits(cfg, a.N) || a.dot_cols == nullptr)
