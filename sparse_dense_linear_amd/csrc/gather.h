@@ -291,6 +291,48 @@ __device__ inline void accumulate(const Batch<S> &bt, int u, bool on,
     axpy<S>(bt.buf[u], bt.v[u], on, acc);
 }
 
+// Two entries of one row at once, for bf16 B with zeroed slots: for each
+// column, the two entries' elements of B are paired in one register (a
+// byte permute) and added in with one v_dot2 (bf16 x bf16 products, exact,
+// summed into the fp32 accumulator): two instructions per two products
+// instead of four (two widenings, two multiply-adds).  Each dot pairs the
+// same column of two entries, so a non-finite element stays in its column,
+// and a zeroed slot's -0 x +0 adds -0.  Its rounding is not a single one:
+// over 2^20 random cases its error stayed within 2.5 x 2^-24 of
+// |a0 b0| + |a1 b1| + |acc| (two fp32 multiply-adds: within 2 x 2^-24),
+// with denormals kept.  Measured (A/B, one box): pruned 4096-row bf16
+// product 46.3 -> 43.4 us, skewed bf16 6.69 -> 6.45 ms.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <class S>
+constexpr bool kPairDot = kSlotsZeroed<S> && (S::VEC == 2 || S::VEC == 4 || S::VEC == 8) &&
+                          S::U % 2 == 0;
+
+template <class S>
+__device__ inline void accumulate_two(const Batch<S> &bt, int u, float (&acc)[S::NV][S::VEC])
+{
+    constexpr int D = S::VEC / 2;  // 32-bit words (column pairs) per vector
+    // the two values as one bf16 pair: entry u low, entry u+1 high
+    const uint32_t vv = __builtin_amdgcn_perm(__float_as_uint(bt.v[u + 1]),
+                                              __float_as_uint(bt.v[u]), 0x07060302u);
+    const bf16x2_t vp = __builtin_bit_cast(bf16x2_t, vv);
+#pragma unroll
+    for (int k = 0; k < S::NV; ++k) {
+        uint32_t w0[D], w1[D];
+        __builtin_memcpy(w0, &bt.buf[u][k], sizeof(w0));
+        __builtin_memcpy(w1, &bt.buf[u + 1][k], sizeof(w1));
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const bf16x2_t lo = __builtin_bit_cast(bf16x2_t,
+                __builtin_amdgcn_perm(w1[d], w0[d], 0x05040100u));
+            const bf16x2_t hi = __builtin_bit_cast(bf16x2_t,
+                __builtin_amdgcn_perm(w1[d], w0[d], 0x07060302u));
+            acc[k][2 * d] = __builtin_amdgcn_fdot2_f32_bf16(lo, vp, acc[k][2 * d], false);
+            acc[k][2 * d + 1] = __builtin_amdgcn_fdot2_f32_bf16(hi, vp, acc[k][2 * d + 1], false);
+        }
+    }
+}
+
 // Group-local SAXPY over entries first .. first+cnt-1 of a chunk held one
 // per lane (lane k: column `col`, value `val`), read by lane shuffles:
 // acc += val * B[col, this lane's columns], U gathers at a time.
@@ -313,9 +355,15 @@ __device__ inline void consume_lanes(int32_t col, float val, int first, int cnt,
             for (int k = 0; k < S::NV; ++k)
                 bt.buf[u][k] = load_slot_vec<S>(src, c, row_bytes, lc, k, on);
         }
+        if constexpr (kPairDot<S>) {
 #pragma unroll
-        for (int x = 0; x < S::U; ++x)
-            accumulate<S>(bt, x, x < n, acc);
+            for (int x = 0; x < S::U; x += 2)
+                accumulate_two<S>(bt, x, acc);
+        } else {
+#pragma unroll
+            for (int x = 0; x < S::U; ++x)
+                accumulate<S>(bt, x, x < n, acc);
+        }
     }
 }
 
