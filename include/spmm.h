@@ -56,12 +56,18 @@
  * rowptr[M] - rowptr[0] < 2^31.  spmm_last_error() gives a text for the most
  * recent failure on the calling thread.
  *
- * Numerics: products and sums are carried in fp32 (bf16 inputs are widened
- * exactly to fp32 first) with fused multiply-adds, in an order that differs
- * from the sequential one.  Rows handled by one wavefront are bitwise
- * repeatable from run to run; rows long enough to be split across
- * wavefronts are reduced with fp32 atomic adds, whose order (and so the last
- * bits) can differ between runs.
+ * Numerics: products and sums are carried in fp32 with fused multiply-adds,
+ * in an order that differs from the sequential one.  bf16 inputs: the
+ * products of two bf16 values are exact in fp32; rows taken by a whole
+ * wavefront (medium rows, chunks of long rows) add two entries' products
+ * per column with one bf16 dot-product instruction into the fp32
+ * accumulator (its rounding error stays within that of two fp32
+ * multiply-adds plus a quarter), other rows widen each element exactly and
+ * use fused multiply-adds.  Infinities and NaN in B or vals reach exactly
+ * the elements of C that IEEE arithmetic sends them to.  Rows handled by
+ * one wavefront are bitwise repeatable from run to run; rows long enough
+ * to be split across wavefronts are reduced with fp32 atomic adds, whose
+ * order (and so the last bits) can differ between runs.
  */
 #ifndef SDL_SPMM_H
 #define SDL_SPMM_H
