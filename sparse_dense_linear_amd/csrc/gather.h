@@ -120,21 +120,6 @@ struct WaveStage {
     uint8_t rid[kShortCap];   // row of the entry within its tile
 };
 
-
-// Exclusive prefix sum of v over the 64 lanes of the wavefront.
-__device__ inline int wave_exclusive_sum(int v)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    int x = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off)
-            x += y;
-    }
-    return x - v;
-}
-
 template <int DT> __device__ inline float load_val(const void *vals, int64_t p);
 template <> __device__ inline float load_val<SPMM_DTYPE_F32>(const void *vals, int64_t p)
 { return ((const float *)vals)[p]; }
@@ -460,6 +445,11 @@ template <class S, bool ATOMIC>
 __device__ inline void emit_row(float *C, int64_t row, int64_t N, int64_t col0,
                                 int j, const float (&acc)[S::NV][S::VEC])
 {
+    // The lane's addresses are formed here at every call rather than kept
+    // live across the caller's loops (they cost registers there, and the
+    // spills a 128-register wavefront would need cost more than the few
+    // instructions).
+    __asm__ volatile("" : "+v"(j));
     float *crow = C + row * N + col0;
 #pragma unroll
     for (int k = 0; k < S::NV; ++k) {

@@ -7,6 +7,23 @@
 
 namespace sdl {
 
+// Exclusive prefix sum over the 64 lanes of a wavefront (lane l gets the sum
+// of lanes 0 .. l-1), by DPP moves, which need no lane-address registers:
+// shifts right by 1, 2, 4, 8 within each row of 16 lanes (lanes with no
+// source add 0), then lane 15 of rows 0 and 2 into rows 1 and 3, then lane
+// 31 into rows 2 and 3.  Called by all 64 lanes.
+__device__ inline int wave_exclusive_sum(int v)
+{
+    int x = v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return x - v;
+}
+
 constexpr int kWave = 64;            // CDNA wavefront width
 constexpr int kWavesPerBlock = 4;    // worker block = 256 threads
 constexpr int kBlock = kWave * kWavesPerBlock;

@@ -181,14 +181,8 @@ __device__ inline int wave_sum_i(int v)
 
 __device__ inline int wave_excl_scan_i(int v, int lane)
 {
-    int x = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off)
-            x += y;
-    }
-    return x - v;
+    (void)lane;
+    return wave_exclusive_sum(v);
 }
 
 // The kPlanLaneRows consecutive rows of this lane in a round starting at
