@@ -23,9 +23,9 @@ K = 2000
 BF16_BITS = {"inf": 0x7F80, "-inf": 0xFF80, "nan": 0x7FC0}
 
 
-def problem(dtype, N, seed):
+def problem(dtype, N, seed, K=K, M=3000):
     rng = np.random.default_rng(seed)
-    lengths = rng.choice([0, 1, 2, 3, 5, 7, 9, 12, 30, 100, 700, 1500], size=3000,
+    lengths = rng.choice([0, 1, 2, 3, 5, 7, 9, 12, 30, 100, 700, 1500], size=M,
                          p=[.05, .1, .1, .1, .1, .1, .1, .1, .1, .08, .05, .02])
     p = W.rows_with_lengths(lengths, K, N, seed=seed, dtype=dtype)
     # one special value in about 5 % of the rows of B, at a random column
@@ -75,3 +75,15 @@ def test_special_values_stay_in_their_columns(dtype, N):
     torch.cuda.synchronize()
     assert sdl.stream_faults() == 0
     check(C.cpu().numpy().reshape(p.M, p.N), p, f"{dtype} N={N} element-balanced")
+
+
+def test_special_values_pair_form():
+    """B of 307 MB with rows of 512 bytes (bf16, N = 256): the PAIR form, two
+    medium rows per item, one column half each."""
+    p = problem("bf16", 256, seed=97, K=600_000, M=2000)
+    args = dev_arrays(p)
+    C = torch.full((p.M * p.N,), 7.0, dtype=torch.float32, device="cuda")
+    sdl.spmm_csr_bf16in_f32acc(*args, C, p.M, p.K, p.N)
+    torch.cuda.synchronize()
+    assert sdl.stream_faults() == 0
+    check(C.cpu().numpy().reshape(p.M, p.N), p, "bf16 N=256 PAIR form")
