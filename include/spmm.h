@@ -284,8 +284,10 @@ spmm_status_t spmm_csr_eb(int32_t dtype, const int32_t *rowptr,
  *
  * Ownership, asynchrony and errors as for the product.  nnz == 0 returns
  * at once; N == 0 with stored entries is UNSUPPORTED.  Numerics: products
- * and sums in fp32 with fused multiply-adds, in an order that differs from
- * the sequential one; bf16 operands are widened exactly.  Every value is
+ * and sums in fp32, in an order that differs from the sequential one: fp32
+ * operands with fused multiply-adds; bf16 operands (N a multiple of 8) by
+ * bf16 dot-product instructions over pairs of neighbouring columns (exact
+ * products, fp32 sums), other bf16 widths widened exactly.  Every value is
  * computed by one wavefront, so results repeat bit for bit.
  */
 spmm_status_t sddmm_csr_f32(const int32_t *rowptr, const int32_t *colind,

@@ -358,9 +358,11 @@ __device__ inline void consume_lanes(int32_t col, float val, int first, int cnt,
 // order (a chain of fused multiply-adds per vector, vectors past the end of
 // the row left out), then a butterfly over the group's G lanes adds the
 // parts.  This is the SDDMM kernel's order when the two use the same group
-// width, so the value is the SDDMM value bit for bit.
+// width, so the value is the SDDMM value bit for bit.  bf16 vectors of 8:
+// the chain is one v_dot2 per pair of neighbouring columns (both operands
+// bf16, exact products, fp32 sum), as in the SDDMM kernel.
 template <class S>
-__device__ inline float group_dot(const float (&x)[S::NV][S::VEC],
+__device__ inline float group_dot(const typename BLoad<S::DT, S::VEC>::raw (&x)[S::NV],
                                   const typename BLoad<S::DT, S::VEC>::raw (&y)[S::NV],
                                   const LaneCols<S> &lc)
 {
@@ -368,12 +370,24 @@ __device__ inline float group_dot(const float (&x)[S::NV][S::VEC],
     float d = 0.0f;
 #pragma unroll
     for (int k = 0; k < S::NV; ++k) {
-        float yv[S::VEC];
-        L::widen(y[k], yv);
         float dk = 0.0f;
+        if constexpr (S::DT == SPMM_DTYPE_BF16 && S::VEC == 8) {
+            uint32_t xw[4], yw[4];
+            __builtin_memcpy(xw, &x[k], sizeof(xw));
+            __builtin_memcpy(yw, &y[k], sizeof(yw));
 #pragma unroll
-        for (int e = 0; e < S::VEC; ++e)
-            dk = fmaf(x[k][e], yv[e], dk);
+            for (int q = 0; q < 4; ++q)
+                dk = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xw[q]),
+                                                     __builtin_bit_cast(bf16x2_t, yw[q]),
+                                                     dk, false);
+        } else {
+            float xv[S::VEC], yv[S::VEC];
+            L::widen(x[k], xv);
+            L::widen(y[k], yv);
+#pragma unroll
+            for (int e = 0; e < S::VEC; ++e)
+                dk = fmaf(xv[e], yv[e], dk);
+        }
         d += lc.live[k] ? dk : 0.0f;
     }
 #pragma unroll
@@ -382,15 +396,17 @@ __device__ inline float group_dot(const float (&x)[S::NV][S::VEC],
     return d;
 }
 
-// This lane's columns of row `row` of the M x N row operand (flat address).
+// This lane's columns of row `row` of the M x N row operand (flat address),
+// as loaded.
 template <class S>
 __device__ inline void load_x_row(const char *X, int64_t row, uint32_t row_bytes,
-                                  const LaneCols<S> &lc, float (&x)[S::NV][S::VEC])
+                                  const LaneCols<S> &lc,
+                                  typename BLoad<S::DT, S::VEC>::raw (&x)[S::NV])
 {
     typedef BLoad<S::DT, S::VEC> L;
 #pragma unroll
     for (int k = 0; k < S::NV; ++k)
-        L::widen(L::load(X + (uint64_t)row * row_bytes + lc.ofs[k]), x[k]);
+        x[k] = L::load(X + (uint64_t)row * row_bytes + lc.ofs[k]);
 }
 
 // FusedMM over entries first .. first+cnt-1 of a chunk held one per lane
@@ -401,7 +417,7 @@ template <class S>
 __device__ inline void consume_lanes_fused(int32_t col, int first, int cnt,
                                            const BSrc &dsrc, const BSrc &ysrc,
                                            uint32_t row_bytes, const LaneCols<S> &lc,
-                                           const float (&x)[S::NV][S::VEC],
+                                           const typename BLoad<S::DT, S::VEC>::raw (&x)[S::NV],
                                            float (&acc)[S::NV][S::VEC])
 {
     typedef typename BLoad<S::DT, S::VEC>::raw Raw;

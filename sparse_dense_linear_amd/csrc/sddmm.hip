@@ -42,6 +42,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // VEC consecutive elements of a dense row, widened exactly to fp32.
 template <int DT, int VEC> struct RowLoad;
@@ -111,20 +112,45 @@ __device__ inline void dots(const void *__restrict__ C, const void *__restrict__
         const bool in = c < N;
         const int64_t cc = in ? c : N - S::VEC;
         constexpr int NC = ONE_ROW ? 1 : NU;
-        float cv[NC][S::VEC], bv[NU][S::VEC];
+        if constexpr (S::DT == SPMM_DTYPE_BF16 && S::VEC == 8) {
+            // bf16: one v_dot2 per pair of neighbouring columns (exact
+            // products, fp32 sum), on the words as loaded
+            u32x4 cw[NC], bw[NU];
 #pragma unroll
-        for (int u = 0; u < NC; ++u)
-            RowLoad<S::DT, S::VEC>::load(C, ci[u] + cc, cv[u]);
+            for (int u = 0; u < NC; ++u)
+                cw[u] = *(const u32x4 *)((const uint16_t *)C + ci[u] + cc);
 #pragma unroll
-        for (int u = 0; u < NU; ++u)
-            RowLoad<S::DT, S::VEC>::load(B, bj[u] + cc, bv[u]);
+            for (int u = 0; u < NU; ++u)
+                bw[u] = *(const u32x4 *)((const uint16_t *)B + bj[u] + cc);
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            float d = 0.0f;
+            for (int u = 0; u < NU; ++u) {
+                const u32x4 c4 = cw[ONE_ROW ? 0 : u];
+                const uint32_t cq[4] = {c4.x, c4.y, c4.z, c4.w};
+                const uint32_t bq[4] = {bw[u].x, bw[u].y, bw[u].z, bw[u].w};
+                float d = 0.0f;
 #pragma unroll
-            for (int x = 0; x < S::VEC; ++x)
-                d = __builtin_fmaf(cv[ONE_ROW ? 0 : u][x], bv[u][x], d);
-            part[u] += in ? d : 0.0f;
+                for (int q = 0; q < 4; ++q)
+                    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, cq[q]),
+                                                        __builtin_bit_cast(bf16x2_t, bq[q]),
+                                                        d, false);
+                part[u] += in ? d : 0.0f;
+            }
+        } else {
+            float cv[NC][S::VEC], bv[NU][S::VEC];
+#pragma unroll
+            for (int u = 0; u < NC; ++u)
+                RowLoad<S::DT, S::VEC>::load(C, ci[u] + cc, cv[u]);
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+                RowLoad<S::DT, S::VEC>::load(B, bj[u] + cc, bv[u]);
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                float d = 0.0f;
+#pragma unroll
+                for (int x = 0; x < S::VEC; ++x)
+                    d = __builtin_fmaf(cv[ONE_ROW ? 0 : u][x], bv[u][x], d);
+                part[u] += in ? d : 0.0f;
+            }
         }
     }
 }

@@ -83,7 +83,7 @@ __device__ inline void wave_range(const WorkerArgs &a, int lane, int g,
                                   float (&acc)[S::NV][S::VEC])
 {
     zero_acc<S>(acc);
-    float x[S::NV][S::VEC];
+    typename BLoad<S::DT, S::VEC>::raw x[S::NV];
     if constexpr (S::FUSED)
         load_x_row<S>((const char *)a.dot_rows, row, row_bytes, lc, x);
     // positions past the range read the range's last entry (valid address)
@@ -262,13 +262,8 @@ __device__ inline void issue_fused(Batch<S> &bt, const WaveStage &ws,
         }
     }
 #pragma unroll
-    for (int u = 0; u < S::U; ++u) {
-        float x[S::NV][S::VEC];
-#pragma unroll
-        for (int k = 0; k < S::NV; ++k)
-            L::widen(xb[u][k], x[k]);
-        bt.v[u] = group_dot<S>(x, yb[u], lc);
-    }
+    for (int u = 0; u < S::U; ++u)
+        bt.v[u] = group_dot<S>(xb[u], yb[u], lc);
 }
 
 // One short tile: rows r0 .. r0+T-1 with T = P*R; group g owns rows
