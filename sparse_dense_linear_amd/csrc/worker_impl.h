@@ -719,6 +719,10 @@ void call_kernel(WorkerArgs a, ProductShape ps)
     const int64_t hub_base = s_lo * n_hub + k;
     const int64_t n_xh = (s_hi - s_lo) * n_hub;          // the XCD's hub chunks
     const int64_t n_qh = n_xh > k ? (n_xh - k + 7) / 8 : 0;  // this queue's
+    // A call whose every item was a static tile grabs nothing (the uniform
+    // 1024-row workload).
+    if (n_hub == 0 && n_med == 0 && n_dyn == 0)
+        return;
     // Lane 0 holds the next grabbed index; it is read (and waited for) only
     // at the top of the next round, so the grab overlaps the current item.
     uint32_t next = 0;
