@@ -167,10 +167,13 @@ def cpu_baseline(p, budget_s: float = 10.0, op: str = "spmm", dense=None) -> dic
 
 def gather_ceiling(torch, dev) -> dict:
     """Bandwidth of the bare access pattern: output row i = sum of D random
-    rows of B (D gathers of N fp32 + one row store per output row), for a B
-    the size of the power-law workload's (67 MB, fits the Infinity Cache)
-    and one 16x larger (1 GiB, does not), and of a 1 GiB device copy.
-    Bytes counted: gathers + index reads + C writes (copy: read + write)."""
+    rows of B (D gathers of N fp32 + one row store per output row), for
+    256-byte rows (N = 64) from a B the size of the power-law workload's
+    (67 MB, fits the Infinity Cache) and one 16x larger (1 GiB, does not);
+    for 1 KB rows (N = 256: the pruned and skewed workloads' row size) from
+    a B of 4 MB (fits each XCD's L2) and of 1 GiB; and of a 1 GiB device
+    copy.  Bytes counted: gathers + index reads + C writes (copy: read +
+    write)."""
     import ctypes
     from sparse_dense_linear_amd import build as B_
     lib = ctypes.CDLL(B_.CEILING_PATH)
@@ -179,7 +182,7 @@ def gather_ceiling(torch, dev) -> dict:
                                        ctypes.c_void_p]
     lib.sdl_gather_ceiling.restype = ctypes.c_int
     stream = torch.cuda.current_stream(dev)
-    N, M, reps = 64, 262144, 20
+    reps = 20
 
     def timed(fn):
         for _ in range(3):
@@ -193,11 +196,13 @@ def gather_ceiling(torch, dev) -> dict:
         e1.synchronize()
         return e0.elapsed_time(e1) / reps * 1e-3
 
-    out = {"kernel": "gather_rows (ceiling.hip)", "N": N, "M": M, "reps": reps,
-           "runs": []}
-    for K in (262144, 4194304):
+    out = {"kernel": "gather_rows (ceiling.hip)", "reps": reps, "runs": []}
+    for N, M, K, Ds in ((64, 262144, 262144, (1, 2, 4, 8)),
+                        (64, 262144, 4194304, (1, 2, 4, 8)),
+                        (256, 65536, 4096, (4, 8, 16)),
+                        (256, 65536, 1048576, (4, 8, 16))):
         Bm = torch.randn(K * N, dtype=torch.float32, device=dev)
-        for D in (1, 2, 4, 8):
+        for D in Ds:
             idx = torch.randint(0, K, (M * D,), dtype=torch.int32, device=dev)
             C = torch.empty(M * N, dtype=torch.float32, device=dev)
 
@@ -208,8 +213,8 @@ def gather_ceiling(torch, dev) -> dict:
                     raise RuntimeError(f"sdl_gather_ceiling returned {rc}")
             t = timed(run)
             nbytes = M * D * N * 4 + M * D * 4 + M * N * 4
-            out["runs"].append({"B_bytes": K * N * 4, "D": D, "us": round(t * 1e6, 2),
-                                "GBps": round(nbytes / t / 1e9, 1)})
+            out["runs"].append({"N": N, "M": M, "B_bytes": K * N * 4, "D": D,
+                                "us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1)})
         del Bm
     a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)

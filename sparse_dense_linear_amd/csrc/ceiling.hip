@@ -79,6 +79,7 @@ extern "C" int sdl_gather_ceiling(const float *B, const int32_t *idx, float *C,
     case 2: err = launch<2>(B, idx, C, M, N, s); break;
     case 4: err = launch<4>(B, idx, C, M, N, s); break;
     case 8: err = launch<8>(B, idx, C, M, N, s); break;
+    case 16: err = launch<16>(B, idx, C, M, N, s); break;
     default: return 1;
     }
     return err == hipSuccess ? 0 : 2;
