@@ -133,7 +133,7 @@ template <> __device__ inline float load_val<SPMM_DTYPE_BF16>(const void *vals, 
 // 3 wavefronts per SIMD measured 5-11 % slower than 8 at 4 (pruned 4096^2,
 // N = 192 and 256), once queues stopped reserving items ahead.
 // PAIR: the product form for a B larger than the Infinity Cache whose rows
-// are two column passes wide: medium rows are taken two at a time, one
+// are two column passes wide: medium rows are taken four at a time, one
 // column half per item (see call_kernel).
 template <int DT_, int VEC_, int G_, int NV_, bool BUF_, bool FUSED_ = false,
           bool PAIR_ = false>

@@ -66,7 +66,7 @@ hipError_t launch_call(const WorkerConfig &cfg, const WorkerArgs &a,
     }
     // B larger than the Infinity Cache, read through a buffer resource, with
     // rows of 512 bytes (two column passes of 16 lanes): the PAIR form
-    // (medium rows two at a time, one column half per item).  Rows of 1 KB
+    // (medium rows four at a time, one column half per item).  Rows of 1 KB
     // keep the one-pass form: the skewed bf16 workload (N = 512), whose
     // hub chunks and short tiles would then take two column passes each,
     // was 5 % slower in the PAIR form.

@@ -162,26 +162,6 @@ __device__ inline bool medium_ready(const WorkerArgs &a, int64_t i, int64_t *row
     return true;
 }
 
-// Rows of medium entries 2u and 2u + 1 (the second -1 when 2u + 1 = n_med)
-// if both are published: both words are read by one load.  Never waits.
-__device__ inline bool medium_pair_ready(const WorkerArgs &a, int64_t u, int64_t n_med,
-                                         int lane, int64_t *ra, int64_t *rb)
-{
-    const int64_t m = 2 * u + (lane & 1);
-    const uint64_t w = m < n_med ? tag_load(a.plan.medium_rows + m) : 0;
-    const uint64_t wa = __shfl(w, 0), wb = __shfl(w, 1);
-    if (!tag_is(wa, a.epoch))
-        return false;
-    if (2 * u + 1 < n_med) {
-        if (!tag_is(wb, a.epoch))
-            return false;
-        *rb = (uint32_t)wb;
-    } else {
-        *rb = -1;
-    }
-    *ra = (uint32_t)wa;
-    return true;
-}
 
 // Add one column pass of a row's partial sums into C with device atomics.
 // After reduce_groups every group holds the sums; group 0 lays each of its
@@ -407,19 +387,44 @@ __device__ inline bool hub_ready(const WorkerArgs &a, int64_t l, int64_t *row)
     return true;
 }
 
-// Two medium rows ra and rb (rb < 0: none) in one wavefront, over the
-// column pass starting at col0: lanes [0, 32) load ra's entries and lanes
-// [32, 64) rb's, groups [0, R/2) consume the first half of the lanes and the
-// others the second, and each half is reduced and stored on its own.  Both
-// rows are medium rows, so each holds at least one entry.
-template <class S>
-__device__ void do_pair(const WorkerArgs &a, int lane, int g, int j, int64_t ra,
-                        int64_t rb, int64_t col0, const BSrc &src, uint32_t row_bytes)
+
+// PAIR form items: medium rows 4u .. 4u+3 of the list, one row per 16-lane
+// group.  Whether all of the item's plan words are published, and this
+// lane's group's row (-1 past the end of the list).  Never waits.
+struct QuadRow {
+    bool ok;
+    int64_t row;   // this lane's group's row, -1 past the list
+};
+__device__ inline QuadRow medium_quad_ready(const WorkerArgs &a, int64_t u, int64_t n_med,
+                                            int lane, int g)
 {
-    static_assert(S::PAIR && S::R >= 2 && S::NV == 1 && !S::FUSED, "pair shapes only");
-    constexpr int H = kWave / 2;
-    const bool upper = lane >= H;
-    const int64_t row = upper ? rb : ra;
+    const int64_t m = 4 * u + (lane & 3);
+    const uint64_t w = (lane < 4 && m < n_med) ? tag_load(a.plan.medium_rows + m) : 0;
+    bool ok = true;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint64_t wt = __shfl(w, t);
+        if (4 * u + t < n_med && !tag_is(wt, a.epoch))
+            ok = false;
+    }
+    const uint64_t wg = __shfl(w, g);
+    QuadRow q;
+    q.ok = ok;
+    q.row = 4 * u + g < n_med ? (int64_t)(uint32_t)wg : -1;
+    return q;
+}
+
+// One PAIR form item: group g accumulates its row over the column pass
+// starting at col0 (its entries 16 at a time, one per lane of the group, read
+// by shuffles within the group) and stores it.  Four rows per item instead
+// of two (each then split over two groups) measured 6.43 -> 6.12 ms on the
+// banded workload (A/B, one box): the item's plan words, row bounds and
+// first entries are one round of loads for four rows.
+template <class S>
+__device__ void do_quad(const WorkerArgs &a, int lane, int g, int j, int64_t row,
+                        int64_t col0, const BSrc &src, uint32_t row_bytes)
+{
+    static_assert(S::PAIR && S::R == 4 && S::NV == 1 && !S::FUSED, "PAIR shapes only");
     const bool has = row >= 0;
     int64_t p0 = 0, p1 = 0;
     if (has) {
@@ -427,22 +432,17 @@ __device__ void do_pair(const WorkerArgs &a, int lane, int g, int j, int64_t ra,
         p1 = a.rowptr[row + 1];
     }
     const int len = (int)(p1 - p0);
-    const int len_a = __shfl(len, 0), len_b = __shfl(len, H);
-    const int longest = len_a > len_b ? len_a : len_b;
-    const int n_chunks = (longest + H - 1) / H;
-    const int hl = lane & (H - 1);
-    // the group's row: the lower or the upper half of the lanes
-    const bool g_upper = g >= S::R / 2;
-    const int g_len = g_upper ? len_b : len_a;
-    const int g_first = g * S::G - (g_upper ? H : 0);  // within its half
+    int longest = len;
+    longest = max(longest, __shfl_xor(longest, 16));
+    longest = max(longest, __shfl_xor(longest, 32));
+    const int n_chunks = (longest + S::G - 1) / S::G;
     const LaneCols<S> lc = lane_cols<S>(a.N, col0, j);
     float acc[S::NV][S::VEC];
     zero_acc<S>(acc);
-    // positions past a row read its last entry (valid address)
     int32_t nc = 0;
     float nvv = 0.0f;
     if (has) {
-        const int64_t p = p0 + hl < p1 ? p0 + hl : p1 - 1;
+        const int64_t p = p0 + j < p1 ? p0 + j : p1 - 1;
         nc = a.colind[p];
         nvv = load_val<S::DT>(a.vals, p);
     }
@@ -450,25 +450,17 @@ __device__ void do_pair(const WorkerArgs &a, int lane, int g, int j, int64_t ra,
         const int32_t col = nc;
         const float val = nvv;
         if (c + 1 < n_chunks && has) {
-            const int64_t p = p0 + (int64_t)(c + 1) * H + hl;
+            const int64_t p = p0 + (int64_t)(c + 1) * S::G + j;
             const int64_t q = p < p1 ? p : p1 - 1;
             nc = a.colind[q];
             nvv = load_val<S::DT>(a.vals, q);
         }
-        int cnt = g_len - c * H - g_first;
+        int cnt = len - c * S::G;
         cnt = cnt < 0 ? 0 : (cnt > S::G ? S::G : cnt);
         consume_lanes<S>(col, val, g * S::G, cnt, src, row_bytes, lc, acc);
     }
-    // each half's groups add up their partial rows
-#pragma unroll
-    for (int off = S::G; off < H; off <<= 1)
-#pragma unroll
-        for (int x = 0; x < S::VEC; ++x)
-            acc[0][x] += __shfl_xor(acc[0][x], off);
-    if (g == 0 && ra >= 0)
-        emit_row<S, false>(a.C, ra, a.N, col0, j, acc);
-    if (g == S::R / 2 && rb >= 0)
-        emit_row<S, false>(a.C, rb, a.N, col0, j, acc);
+    if (has)
+        emit_row<S, false>(a.C, row, a.N, col0, j, acc);
 }
 
 // Polls for a plan word, at most `polls` times.  The plan blocks are the
@@ -735,15 +727,15 @@ void call_kernel(WorkerArgs a, ProductShape ps)
         do_hub<S>(a, ws, lane, g, j, hub_base + 8 * i, n_hub, src, ysrc, row_bytes);
         i = __builtin_amdgcn_readfirstlane(next);
     }
-    // PAIR form: then the medium rows, two consecutive ones per item and
+    // PAIR form: then the medium rows, four consecutive ones per item and
     // one column half per item.  XCDs 0-3 take the first half of B's
     // columns and XCDs 4-7 the second, each XCD a contiguous quarter of the
-    // pairs in row order (its 8 queues interleaved), so the rows of B that
+    // items in row order (its 8 queues interleaved), so the rows of B that
     // neighbouring rows gather (a band) are read from that XCD's L2 at half
     // the width: a window of B rows twice as tall fits it.
     int64_t n_qp = 0;
     if constexpr (S::PAIR) {
-        const int64_t n_pairs = (n_med + 1) / 2;
+        const int64_t n_pairs = (n_med + 3) / 4;   // items: four rows each
         const int64_t u_lo = (int64_t)(x & 3) * n_pairs / 4;
         const int64_t u_hi = (int64_t)((x & 3) + 1) * n_pairs / 4;
         n_qp = u_hi - u_lo > k ? (u_hi - u_lo - k + 7) / 8 : 0;
@@ -754,10 +746,14 @@ void call_kernel(WorkerArgs a, ProductShape ps)
             const int64_t u = u_lo + k + 8 * (i - n_qh);
             if (pahead && lane == 0)
                 next = atomicAdd(ctr, 1u);
-            int64_t ra = -1, rb = -1;
-            if (wait_for(a.wait_polls,
-                         [&]() { return medium_pair_ready(a, u, n_med, lane, &ra, &rb); }))
-                do_pair<S>(a, lane, g, j, ra, rb, col0, src, row_bytes);
+            QuadRow qr;
+            qr.ok = false;
+            qr.row = -1;
+            if (wait_for(a.wait_polls, [&]() {
+                    qr = medium_quad_ready(a, u, n_med, lane, g);
+                    return qr.ok;
+                }))
+                do_quad<S>(a, lane, g, j, qr.row, col0, src, row_bytes);
             else
                 note_fault(a, lane);
             if (!pahead && lane == 0)

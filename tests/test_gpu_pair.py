@@ -1,12 +1,13 @@
 """The PAIR form of the product: with B larger than the Infinity Cache and
 rows of B of 512 bytes (fp32 N = 128, bf16 N = 256), medium rows are taken
-two at a time, one column half per item, each half on its own four XCDs.
-These cases use such a B (600,000 rows, 307 MB) with few rows of A, so the
-oracle stays quick: an odd number of medium rows (the last pair has one
-row), pairs of very different lengths, medium rows between short, long
-and hub rows (pairs of rows that are not neighbours), empty rows, columns
-in any order, a row-block view, and a banded matrix (the case the form is
-for).  Every element against the oracle, C NaN-filled, fault count read."""
+four at a time (one 16-lane group each), one column half per item, each
+half on its own four XCDs.  These cases use such a B (600,000 rows,
+307 MB) with few rows of A, so the oracle stays quick: 1, 2, 3 and 5
+medium rows (items with fewer than four rows), rows of very different
+lengths in one item, medium rows between short, long and hub rows (items
+of rows that are not neighbours), empty rows, columns in any order, a
+row-block view, and a banded matrix (the case the form is for).  Every
+element against the oracle, C NaN-filled, fault count read."""
 import numpy as np
 import pytest
 import torch
@@ -49,17 +50,18 @@ def test_pair_form_mixed_rows(dtype):
 
 
 def test_pair_form_odd_and_shuffled():
-    """Columns in no order within rows, and exactly one medium row (a pair
-    with no second row)."""
+    """Columns in no order within rows, and 1, 2, 3 or 5 medium rows (items
+    with fewer than four rows)."""
     p = mixed("f32", seed=83, M=1500, shuffle=True)
     Cref, Sref = reference(p)
     assert_parity(run_gpu(p), Cref, Sref, "f32", "pair shuffled")
-    lengths = np.zeros(40, np.int64)
-    lengths[7] = 50
-    q = W.rows_with_lengths(lengths, K_BIG, 128, seed=84)
-    assert compare_plan(q)["n_medium"] == 1
-    Cref, Sref = reference(q)
-    assert_parity(run_gpu(q), Cref, Sref, "f32", "one medium row")
+    for n_medium in (1, 2, 3, 5):
+        lengths = np.zeros(40, np.int64)
+        lengths[[7, 8, 20, 21, 33][:n_medium]] = [50, 300, 90, 41, 200][:n_medium]
+        q = W.rows_with_lengths(lengths, K_BIG, 128, seed=84 + n_medium)
+        assert compare_plan(q)["n_medium"] == n_medium
+        Cref, Sref = reference(q)
+        assert_parity(run_gpu(q), Cref, Sref, "f32", f"{n_medium} medium rows")
 
 
 def test_pair_form_banded_view():
