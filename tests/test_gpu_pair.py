@@ -83,3 +83,26 @@ def test_pair_form_banded_view():
     Cref, Sref = reference(p, rows=sub)
     assert_parity(C.cpu().numpy().reshape(p.M, p.N)[r0:r1], Cref, Sref, "f32",
                   "pair banded view")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_pair_form_random(seed):
+    """Seeded random cases of the form: M from 1 to 2500, medium rows of
+    any length in any share (items of rows of very different lengths, a
+    last item of one to four rows), short, long and empty rows among them,
+    both element types, default or random thresholds."""
+    rng = np.random.default_rng(700 + seed)
+    dtype = "bf16" if seed % 2 else "f32"
+    M = int(rng.integers(1, 2500))
+    lengths = rng.choice([0, 3, 17, 40, 130, 512, 900], size=M,
+                         p=[.05, .15, .3, .2, .2, .05, .05])
+    p = W.rows_with_lengths(lengths, K_BIG, WIDTH[dtype], seed=700 + seed, dtype=dtype)
+    tuning = None
+    if seed >= 3:
+        short_max = int(rng.choice([0, 4, 16]))
+        tuning = sdl.Tuning(short_max, short_max + int(rng.choice([30, 200, 1000])),
+                            int(rng.choice([64, 512])))
+    plan = compare_plan(p, tuning)
+    Cref, Sref = reference(p)
+    what = f"seed={seed} M={M} {dtype} tuning={tuning} medium={plan['n_medium']}"
+    assert_parity(run_gpu(p, tuning=tuning), Cref, Sref, dtype, what)
