@@ -210,7 +210,7 @@ load_row_vec(const BSrc &src, int32_t row, uint32_t row_bytes,
 // infinities and NaN included, and the accumulation needs no select.
 // Otherwise the slot repeats a valid entry and accumulate() selects the
 // old acc.  Measured (same box, A/B): the pruned 4096-row bf16 product
-// 54.7 -> 47.5 us and the skewed bf16 one 7.15 -> 6.71 ms, where the
+// 53.1 -> 46.1 us and the skewed bf16 one 7.02 -> 6.66 ms, where the
 // widening already costs one instruction per element; for fp32 B the
 // selects-free form was 7-9 % slower (pruned, power-law; the loads past
 // the record count alone cost nothing), so fp32 keeps the selects.

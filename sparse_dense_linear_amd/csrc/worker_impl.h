@@ -387,16 +387,15 @@ __device__ inline bool hub_ready(const WorkerArgs &a, int64_t l, int64_t *row)
     return true;
 }
 
-
 // PAIR form items: medium rows 4u .. 4u+3 of the list, one row per 16-lane
 // group.  Whether all of the item's plan words are published, and this
 // lane's group's row (-1 past the end of the list).  Never waits.
-struct QuadRow {
+struct PairItemRow {
     bool ok;
     int64_t row;   // this lane's group's row, -1 past the list
 };
-__device__ inline QuadRow medium_quad_ready(const WorkerArgs &a, int64_t u, int64_t n_med,
-                                            int lane, int g)
+__device__ inline PairItemRow medium_item_ready(const WorkerArgs &a, int64_t u,
+                                                int64_t n_med, int lane, int g)
 {
     const int64_t m = 4 * u + (lane & 3);
     const uint64_t w = (lane < 4 && m < n_med) ? tag_load(a.plan.medium_rows + m) : 0;
@@ -408,7 +407,7 @@ __device__ inline QuadRow medium_quad_ready(const WorkerArgs &a, int64_t u, int6
             ok = false;
     }
     const uint64_t wg = __shfl(w, g);
-    QuadRow q;
+    PairItemRow q;
     q.ok = ok;
     q.row = 4 * u + g < n_med ? (int64_t)(uint32_t)wg : -1;
     return q;
@@ -421,7 +420,7 @@ __device__ inline QuadRow medium_quad_ready(const WorkerArgs &a, int64_t u, int6
 // banded workload (A/B, one box): the item's plan words, row bounds and
 // first entries are one round of loads for four rows.
 template <class S>
-__device__ void do_quad(const WorkerArgs &a, int lane, int g, int j, int64_t row,
+__device__ void do_pair_item(const WorkerArgs &a, int lane, int g, int j, int64_t row,
                         int64_t col0, const BSrc &src, uint32_t row_bytes)
 {
     static_assert(S::PAIR && S::R == 4 && S::NV == 1 && !S::FUSED, "PAIR shapes only");
@@ -689,7 +688,7 @@ void call_kernel(WorkerArgs a, ProductShape ps)
         note_fault(a, lane);
         n_med = n_long = n_ch = n_hub = 0;
     }
-    // PAIR form: medium rows leave the shared list for the pair items below
+    // PAIR form: medium rows leave the shared list for the PAIR items below
     const int64_t n_med_list = S::PAIR ? 0 : n_med;
     const int64_t n_dyn = n_ch + n_med_list + ps.n_dyn_tiles;
     // One item per grab: consecutive items go to different wavefronts at
@@ -735,9 +734,9 @@ void call_kernel(WorkerArgs a, ProductShape ps)
     // the width: a window of B rows twice as tall fits it.
     int64_t n_qp = 0;
     if constexpr (S::PAIR) {
-        const int64_t n_pairs = (n_med + 3) / 4;   // items: four rows each
-        const int64_t u_lo = (int64_t)(x & 3) * n_pairs / 4;
-        const int64_t u_hi = (int64_t)((x & 3) + 1) * n_pairs / 4;
+        const int64_t n_items = (n_med + 3) / 4;   // four rows each
+        const int64_t u_lo = (int64_t)(x & 3) * n_items / 4;
+        const int64_t u_hi = (int64_t)((x & 3) + 1) * n_items / 4;
         n_qp = u_hi - u_lo > k ? (u_hi - u_lo - k + 7) / 8 : 0;
         const int64_t col0 = (int64_t)(x >> 2) * S::COLS;
         const bool pahead =
@@ -746,14 +745,14 @@ void call_kernel(WorkerArgs a, ProductShape ps)
             const int64_t u = u_lo + k + 8 * (i - n_qh);
             if (pahead && lane == 0)
                 next = atomicAdd(ctr, 1u);
-            QuadRow qr;
-            qr.ok = false;
-            qr.row = -1;
+            PairItemRow ir;
+            ir.ok = false;
+            ir.row = -1;
             if (wait_for(a.wait_polls, [&]() {
-                    qr = medium_quad_ready(a, u, n_med, lane, g);
-                    return qr.ok;
+                    ir = medium_item_ready(a, u, n_med, lane, g);
+                    return ir.ok;
                 }))
-                do_quad<S>(a, lane, g, j, qr.row, col0, src, row_bytes);
+                do_pair_item<S>(a, lane, g, j, ir.row, col0, src, row_bytes);
             else
                 note_fault(a, lane);
             if (!pahead && lane == 0)
