@@ -1119,7 +1119,7 @@ spmm_status_t spmm_plan_export(const int32_t *rowptr, const int32_t *colind,
         const WorkerConfig cfg = choose_worker(SPMM_DTYPE_F32, 1, nullptr, nullptr);
         int64_t dcounts[6];
         if ((err = launch_worker(cfg, wa, stream, nullptr, nullptr)) != hipSuccess ||
-            (err = launch_plan_export(rowptr, colind, M, wa.th, wa.plan, 1, cap,
+            (err = launch_plan_export(rowptr, colind, wa.th, wa.plan, 1, cap,
                                       (int32_t *)(dev_mem + off_med),
                                       (LongRow *)(dev_mem + off_long),
                                       (Chunk *)(dev_mem + off_chunk),

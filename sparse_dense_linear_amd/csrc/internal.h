@@ -241,7 +241,7 @@ struct Chunk {
 // their bounds found by the product's own search over colind.  Enqueued on
 // `stream`.
 hipError_t launch_plan_export(const int32_t *rowptr, const int32_t *colind,
-                              int64_t M, Thresholds th,
+                              Thresholds th,
                               const PlanBuffers &pb, uint32_t epoch,
                               int64_t cap, int32_t *medium_out,
                               LongRow *long_out, Chunk *chunk_out,

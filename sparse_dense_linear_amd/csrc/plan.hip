@@ -52,7 +52,7 @@ __device__ inline int32_t untag(uint64_t w, uint32_t epoch)
 }
 
 __global__ __launch_bounds__(kExportBlock) void plan_export_kernel(
-    const int32_t *__restrict__ rowptr, int64_t M, Thresholds th,
+    const int32_t *__restrict__ rowptr, Thresholds th,
     PlanBuffers pb, uint32_t epoch, int64_t cap, int32_t *medium_out,
     LongRow *long_out, Chunk *chunk_out, int32_t *hub_out, int64_t *counts_out)
 {
@@ -166,7 +166,7 @@ hipError_t launch_worker(const WorkerConfig &cfg, const WorkerArgs &a,
 }
 
 hipError_t launch_plan_export(const int32_t *rowptr, const int32_t *colind,
-                              int64_t M, Thresholds th,
+                              Thresholds th,
                               const PlanBuffers &pb, uint32_t epoch,
                               int64_t cap, int32_t *medium_out,
                               LongRow *long_out, Chunk *chunk_out,
@@ -176,7 +176,7 @@ hipError_t launch_plan_export(const int32_t *rowptr, const int32_t *colind,
     const int64_t n = cap > 1 ? cap : 1;
     const int64_t blocks = (n + kExportBlock - 1) / kExportBlock;
     hipLaunchKernelGGL(plan_export_kernel, dim3((unsigned)blocks),
-                       dim3(kExportBlock), 0, stream, rowptr, M, th, pb, epoch,
+                       dim3(kExportBlock), 0, stream, rowptr, th, pb, epoch,
                        cap, medium_out, long_out, chunk_out, hub_out, counts_out);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || cap == 0 || colind == nullptr)

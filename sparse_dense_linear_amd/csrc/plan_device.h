@@ -206,7 +206,7 @@ __device__ inline LaneRows lane_rows(const PlanCtx &c, int64_t base, int64_t r1)
         const bool valid = rb + k < r1;
         q.start[k] = rp[k];
         q.len[k] = valid ? rp[k + 1] - rp[k] : 0;
-        q.rc[k] = valid ? classify(q.len[k], c.th) : RowClass{0, 0, 0};
+        q.rc[k] = valid ? classify(q.len[k], c.th) : RowClass{0, 0, 0, 0};
     }
     return q;
 }

@@ -420,8 +420,8 @@ __device__ inline PairItemRow medium_item_ready(const WorkerArgs &a, int64_t u,
 // banded workload (A/B, one box): the item's plan words, row bounds and
 // first entries are one round of loads for four rows.
 template <class S>
-__device__ void do_pair_item(const WorkerArgs &a, int lane, int g, int j, int64_t row,
-                        int64_t col0, const BSrc &src, uint32_t row_bytes)
+__device__ void do_pair_item(const WorkerArgs &a, int g, int j, int64_t row, int64_t col0,
+                             const BSrc &src, uint32_t row_bytes)
 {
     static_assert(S::PAIR && S::R == 4 && S::NV == 1 && !S::FUSED, "PAIR shapes only");
     const bool has = row >= 0;
@@ -752,7 +752,7 @@ void call_kernel(WorkerArgs a, ProductShape ps)
                     ir = medium_item_ready(a, u, n_med, lane, g);
                     return ir.ok;
                 }))
-                do_pair_item<S>(a, lane, g, j, ir.row, col0, src, row_bytes);
+                do_pair_item<S>(a, g, j, ir.row, col0, src, row_bytes);
             else
                 note_fault(a, lane);
             if (!pahead && lane == 0)
