@@ -87,3 +87,50 @@ def test_special_values_pair_form():
     torch.cuda.synchronize()
     assert sdl.stream_faults() == 0
     check(C.cpu().numpy().reshape(p.M, p.N), p, "bf16 N=256 PAIR form")
+
+
+def check_values(got, ref, S, tol, what):
+    """NaN and infinities where the fp64 oracle has them (with their signs),
+    every finite value within tol * S + 1e-6."""
+    assert np.isnan(ref).any() and np.isinf(ref).any(), "the case must hold specials"
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), f"{what}: NaN pattern"
+    inf = np.isinf(ref)
+    assert np.array_equal(np.isinf(got), inf), f"{what}: Inf pattern"
+    assert np.array_equal(np.sign(got[inf]), np.sign(ref[inf])), f"{what}: Inf sign"
+    fin = np.isfinite(ref)
+    err = np.abs(got[fin].astype(np.float64) - ref[fin])
+    assert np.all(err <= tol * S[fin] + ABS), f"{what}: finite values"
+
+
+@pytest.mark.parametrize("dtype,N", [("bf16", 256), ("f32", 64)])
+def test_special_values_sddmm_fusedmm(dtype, N):
+    """SDDMM values and FusedMM rows with infinities and NaN in B: each dot
+    product (bf16: by dot-product instructions over column pairs) is
+    non-finite exactly where IEEE arithmetic makes it so."""
+    p = problem(dtype, N, seed=131 + N, M=1500)
+    rng = np.random.default_rng(131)
+    x = rng.uniform(-1, 1, (p.M, p.N)).astype(np.float32)
+    d = rng.uniform(-1, 1, (p.K, p.N)).astype(np.float32)
+    if dtype == "bf16":
+        x = W.f32_to_bf16_bits(x).reshape(p.M, p.N)
+        d = W.f32_to_bf16_bits(d).reshape(p.K, p.N)
+    def dev(a):
+        a = np.ascontiguousarray(a).reshape(-1)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+    rowptr, colind, _, B = dev_arrays(p)
+    tol = max(1e-5, p.N * 2.0 ** -23)
+    A = torch.full((p.nnz,), 7.0, dtype=torch.float32, device="cuda")
+    fn = sdl.sddmm_csr_f32 if dtype == "f32" else sdl.sddmm_csr_bf16in_f32acc
+    fn(rowptr, colind, dev(x), B, A, p.M, p.K, p.N)
+    torch.cuda.synchronize()
+    assert sdl.stream_faults() == 0
+    Aref, S = oracle.sddmm_ref(p.rowptr, p.colind, x, p.B, p.N)
+    check_values(A.cpu().numpy(), Aref, S, tol, f"sddmm {dtype} N={N}")
+    E = torch.full((p.M * p.N,), 7.0, dtype=torch.float32, device="cuda")
+    fn = sdl.fusedmm_csr_f32 if dtype == "f32" else sdl.fusedmm_csr_bf16in_f32acc
+    fn(rowptr, colind, dev(x), B, dev(d), E, p.M, p.K, p.N, p.nnz)
+    torch.cuda.synchronize()
+    assert sdl.stream_faults() == 0
+    Eref, T = oracle.fusedmm_ref(p.rowptr, p.colind, x, p.B, d, p.N)
+    check_values(E.cpu().numpy().reshape(p.M, p.N), Eref, T, 2 * tol,
+                 f"fusedmm {dtype} N={N}")
