@@ -6,7 +6,8 @@ of medium rows, chunks and hub chunks, element-balanced batches): such a
 slot must leave the accumulator as it is, even when the row of B it would
 otherwise touch holds an infinity, and must not move a non-finite value
 into another column.  Both element types, short/medium/long/hub rows, the
-row-split kernel and the element-balanced kernel."""
+row-split kernel and the element-balanced kernel; SDDMM values and FusedMM
+rows (their bf16 dot products pair neighbouring columns) too."""
 import numpy as np
 import pytest
 import torch
