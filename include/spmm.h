@@ -337,10 +337,15 @@ spmm_status_t fusedmm_csr_f32(const int32_t *rowptr, const int32_t *colind,
 /*
  * FusedMM as fusedmm_csr_f32 with C, B and D given as bf16 bit patterns
  * (uint16), widened exactly to fp32; each value <C_i, B_j> is formed and
- * used in fp32, the sums are fp32, and E is fp32.  One launch; shapes it
- * does not cover (N not a multiple of 8 or above 1024, or C, B, D, E not
- * 16-byte aligned) return SPMM_ERROR_UNSUPPORTED with nothing launched.
- * nnz == 0: E becomes zero.  Other errors and ownership as for the product.
+ * used in fp32, the sums are fp32, and E is fp32.  One launch when N is a
+ * multiple of 8 and at most 1024 and C, B, D and E are 16-byte aligned.
+ * Otherwise C, B and D are first widened into an fp32 copy of (M + 2K) * N
+ * floats, taken from the library's stream-ordered pool and given back on
+ * `stream` once the call's launches are enqueued, and fusedmm_csr_f32 runs
+ * on the copy (same values: bf16 products are exact in fp32);
+ * SPMM_ERROR_OUT_OF_MEMORY if the copy cannot be had.  C, B and D need
+ * 2-byte alignment, E 4-byte.  nnz == 0: E becomes zero.  Other errors and
+ * ownership as for the product.
  */
 spmm_status_t fusedmm_csr_bf16in_f32acc(const int32_t *rowptr,
                                         const int32_t *colind, const uint16_t *C,

@@ -829,9 +829,11 @@ spmm_status_t run_fusedmm(const int32_t *rowptr, const int32_t *colind,
     return st;
 }
 
-// FusedMM with bf16 C, B and D: the one-launch form only (fp32 values and
-// accumulation).  The two-launch route would need a product that weights
-// bf16 rows by fp32 values, which is not built.
+// FusedMM with bf16 C, B and D (fp32 values and accumulation): the
+// one-launch form when the shape allows; otherwise C, B and D are widened
+// exactly into a stream-ordered fp32 copy and the fp32 FusedMM runs on it
+// (the same values: every bf16 product is exact in fp32).  The copy holds
+// (M + 2K) * N floats and is given back on the stream after the call.
 spmm_status_t run_fusedmm_bf16(const int32_t *rowptr, const int32_t *colind,
                                const uint16_t *C, const uint16_t *B,
                                const uint16_t *D, float *E, int64_t M, int64_t K,
@@ -854,12 +856,37 @@ spmm_status_t run_fusedmm_bf16(const int32_t *rowptr, const int32_t *colind,
         return run_with(SPMM_DTYPE_BF16, rowptr, colind, nullptr, nullptr, E, M, 0,
                         N, nullptr, stream_ptr, false, nullptr, nullptr);
     const WorkerConfig cfg = choose_worker(SPMM_DTYPE_BF16, N, D, E);
-    if (!fused_fits(cfg, N) || ((uintptr_t)C) % 16 != 0 || ((uintptr_t)B) % 16 != 0)
-        return fail(SPMM_ERROR_UNSUPPORTED,
-                    "bf16 FusedMM needs N a multiple of 8, at most 1024, and "
-                    "16-byte aligned C, B, D and E");
-    return run_with(SPMM_DTYPE_BF16, rowptr, colind, nullptr, D, E, M, K, N,
-                    nullptr, stream_ptr, false, nullptr, nullptr, false, C, B);
+    if (fused_fits(cfg, N) && ((uintptr_t)C) % 16 == 0 && ((uintptr_t)B) % 16 == 0)
+        return run_with(SPMM_DTYPE_BF16, rowptr, colind, nullptr, D, E, M, K, N,
+                        nullptr, stream_ptr, false, nullptr, nullptr, false, C, B);
+    // widened copy: C at 0, B and D after it, each start 256-byte aligned
+    hipStream_t stream = (hipStream_t)stream_ptr;
+    const auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+    const size_t c_bytes = up((size_t)M * (size_t)N * sizeof(float));
+    const size_t b_bytes = up((size_t)K * (size_t)N * sizeof(float));
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return fail_hip(err, "hipGetDevice");
+    if (test_fail_alloc())
+        return fail(SPMM_ERROR_OUT_OF_MEMORY, "allocation failure forced by SPMM_TEST_FAIL_ALLOC");
+    char *w = nullptr;
+    err = fresh_block(dev, stream, c_bytes + 2 * b_bytes, false, (void **)&w);
+    if (err == hipErrorOutOfMemory)
+        return fail(SPMM_ERROR_OUT_OF_MEMORY, "widened operand allocation failed");
+    if (err != hipSuccess)
+        return fail_hip(err, "widened operand allocation");
+    float *Cw = (float *)w, *Bw = (float *)(w + c_bytes), *Dw = (float *)(w + c_bytes + b_bytes);
+    spmm_status_t st = SPMM_SUCCESS;
+    if ((err = launch_widen_bf16(C, Cw, M * N, stream)) != hipSuccess ||
+        (err = launch_widen_bf16(B, Bw, K * N, stream)) != hipSuccess ||
+        (err = launch_widen_bf16(D, Dw, K * N, stream)) != hipSuccess)
+        st = fail_hip(err, "widen kernel");
+    if (st == SPMM_SUCCESS)
+        st = run_fusedmm(rowptr, colind, Cw, Bw, Dw, E, M, K, N, nnz, stream_ptr);
+    if ((err = hipFreeAsync(w, stream)) != hipSuccess && st == SPMM_SUCCESS)
+        st = fail_hip(err, "hipFreeAsync");
+    return st;
 }
 
 // The element-balanced product: one launch; carry slots in the stream's

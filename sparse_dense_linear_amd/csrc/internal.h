@@ -196,6 +196,10 @@ struct SddmmArgs {
 hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream,
                         hipEvent_t start, hipEvent_t stop);
 
+// Enqueue the exact widening of n bf16 values (bit patterns, 2-byte
+// aligned) to fp32: out[i] = in[i] << 16 as a float.
+hipError_t launch_widen_bf16(const uint16_t *in, float *out, int64_t n, hipStream_t stream);
+
 // One element-balanced product (eb.hip): equal spans of stored entries per
 // wavefront, partial rows at span ends combined through carry slots.
 struct EbArgs {

@@ -321,7 +321,27 @@ hipError_t launch_sd_vec(int group, const SddmmArgs &a, hipStream_t s,
     }
 }
 
+__global__ __launch_bounds__(kBlock) void widen_bf16_kernel(const uint16_t *__restrict__ in,
+                                                           float *__restrict__ out, int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride)
+        out[i] = __uint_as_float((uint32_t)in[i] << 16);
+}
+
 }  // namespace
+
+hipError_t launch_widen_bf16(const uint16_t *in, float *out, int64_t n, hipStream_t stream)
+{
+    if (n <= 0)
+        return hipSuccess;
+    int64_t blocks = (n + kBlock - 1) / kBlock;
+    if (blocks > 8192)
+        blocks = 8192;  // grid-stride beyond that
+    hipLaunchKernelGGL(widen_bf16_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream,
+                       in, out, n);
+    return hipGetLastError();
+}
 
 hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream, hipEvent_t e0,
                         hipEvent_t e1)

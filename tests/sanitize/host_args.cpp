@@ -177,10 +177,10 @@ void sddmm_fusedmm_arguments()
     EXPECT(fusedmm_csr_f32(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 4, 4, 0,
                            nullptr) == SPMM_SUCCESS);
     const uint16_t *h = fake<const uint16_t>();
-    EXPECT(fusedmm_csr_bf16in_f32acc(rp, rp, h, h, h, o, 4, 4, 12, 3, nullptr) ==
-           SPMM_ERROR_UNSUPPORTED);
-    EXPECT(fusedmm_csr_bf16in_f32acc(rp, rp, h, h, h, o, 4, 4, 1032, 3, nullptr) ==
-           SPMM_ERROR_UNSUPPORTED);
+    EXPECT(fusedmm_csr_bf16in_f32acc(rp, rp, h, h, nullptr, o, 4, 4, 12, 3, nullptr) ==
+           SPMM_ERROR_INVALID_VALUE);
+    EXPECT(fusedmm_csr_bf16in_f32acc(rp, rp, h, h, h, fake<float>(2), 4, 4, 1032, 3,
+                                     nullptr) == SPMM_ERROR_INVALID_VALUE);
     EXPECT(fusedmm_csr_bf16in_f32acc(rp, rp, fake<const uint16_t>(1), h, h, o, 4, 4, 8, 3,
                                      nullptr) == SPMM_ERROR_INVALID_VALUE);
 }

@@ -273,15 +273,11 @@ def test_fusedmm_host_validation(M, K, N, nnz, rowptr, E, D, expect):
     (4, 4, 8, 3, FAKE, FAKE, FAKE, None, 1),         # E null
     (4, 4, 8, 3, FAKE, FAKE + 1, FAKE, FAKE, 1),     # C not 2-byte aligned
     (4, 4, 8, 3, FAKE, FAKE, FAKE, FAKE + 2, 1),     # E not 4-byte aligned
-    (4, 4, 12, 3, FAKE, FAKE, FAKE, FAKE, 4),        # N not a multiple of 8
-    (4, 4, 1032, 3, FAKE, FAKE, FAKE, FAKE, 4),      # N above 1024
-    (4, 4, 64, 3, FAKE, FAKE + 2, FAKE, FAKE, 4),    # C not 16-byte aligned
     (0, 4, 8, 0, None, None, None, None, 0),         # M == 0: nothing to do
     (4, 4, 0, 0, None, None, None, None, 0),         # N == 0: nothing to do
 ])
 def test_fusedmm_bf16_host_validation(M, K, N, nnz, rowptr, C, D, E, expect):
-    """bf16 FusedMM refuses bad arguments, and shapes its one launch does not
-    cover, on the host before any HIP call."""
+    """bf16 FusedMM refuses bad arguments on the host before any HIP call."""
     rc = raw_call("fusedmm_csr_bf16in_f32acc", rowptr, FAKE, C, FAKE, D, E, M, K, N,
                   nnz, None)
     assert rc == expect, sdl.lib().spmm_last_error()
@@ -292,6 +288,17 @@ def test_fusedmm_forced_allocation_failure(monkeypatch):
     rc = raw_call("fusedmm_csr_f32", FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 4, 3, None)
     # without a GPU the device query fails first; with one, the forced failure
     assert rc in (2, 3)
+
+
+@pytest.mark.parametrize("N,C", [(12, FAKE), (1032, FAKE), (64, FAKE + 2)])
+def test_fusedmm_bf16_widened_allocation_failure(monkeypatch, N, C):
+    """Shapes outside the one-launch form take the widened copy: its
+    allocation is the first thing after the device query that can fail."""
+    monkeypatch.setenv("SPMM_TEST_FAIL_ALLOC", "1")
+    rc = raw_call("fusedmm_csr_bf16in_f32acc", FAKE, FAKE, C, FAKE, FAKE, FAKE, 4, 4, N,
+                  3, None)
+    assert rc in (2, 3)
+    assert b"SPMM_TEST_FAIL_ALLOC" in sdl.lib().spmm_last_error() or rc == 2
 
 
 def test_sddmm_binding_checks_operands():
