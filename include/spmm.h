@@ -343,7 +343,8 @@ spmm_status_t fusedmm_csr_f32(const int32_t *rowptr, const int32_t *colind,
  * floats, taken from the library's stream-ordered pool and given back on
  * `stream` once the call's launches are enqueued, and fusedmm_csr_f32 runs
  * on the copy (same values: bf16 products are exact in fp32);
- * SPMM_ERROR_OUT_OF_MEMORY if the copy cannot be had.  C, B and D need
+ * SPMM_ERROR_OUT_OF_MEMORY if the copy cannot be had or would pass 2^56
+ * bytes (found before any HIP call).  C, B and D need
  * 2-byte alignment, E 4-byte.  nnz == 0: E becomes zero.  Other errors and
  * ownership as for the product.
  */

@@ -859,7 +859,12 @@ spmm_status_t run_fusedmm_bf16(const int32_t *rowptr, const int32_t *colind,
     if (fused_fits(cfg, N) && ((uintptr_t)C) % 16 == 0 && ((uintptr_t)B) % 16 == 0)
         return run_with(SPMM_DTYPE_BF16, rowptr, colind, nullptr, D, E, M, K, N,
                         nullptr, stream_ptr, false, nullptr, nullptr, false, C, B);
-    // widened copy: C at 0, B and D after it, each start 256-byte aligned
+    // widened copy: C at 0, B and D after it, each start 256-byte aligned;
+    // (M + 2K) * N * 4 can exceed 64 bits for sizes below 2^31, so it is
+    // bounded before anything is sized from it
+    if ((unsigned __int128)(M + 2 * K) * (unsigned __int128)N * sizeof(float) >
+        ((unsigned __int128)1 << 56))
+        return fail(SPMM_ERROR_OUT_OF_MEMORY, "widened operand copy above 2^56 bytes");
     hipStream_t stream = (hipStream_t)stream_ptr;
     const auto up = [](size_t b) { return (b + 255) / 256 * 256; };
     const size_t c_bytes = up((size_t)M * (size_t)N * sizeof(float));

@@ -301,6 +301,16 @@ def test_fusedmm_bf16_widened_allocation_failure(monkeypatch, N, C):
     assert b"SPMM_TEST_FAIL_ALLOC" in sdl.lib().spmm_last_error() or rc == 2
 
 
+def test_fusedmm_bf16_widened_size_bound():
+    """A widened copy whose size would pass 64 bits is refused before any
+    HIP call (no size is computed from a wrapped product)."""
+    big = 2 ** 31 - 1
+    rc = raw_call("fusedmm_csr_bf16in_f32acc", FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, big,
+                  big, 3, None)
+    assert rc == 3, sdl.lib().spmm_last_error()
+    assert b"2^56" in sdl.lib().spmm_last_error()
+
+
 def test_sddmm_binding_checks_operands():
     t = torch.zeros(4, dtype=torch.int32)
     f = torch.zeros(4, dtype=torch.float32)
