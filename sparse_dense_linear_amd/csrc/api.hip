@@ -108,7 +108,7 @@ spmm_status_t resolve(int32_t dtype, int64_t K, int64_t N, const spmm_tuning_t *
         if (req->slab_rows > 0)
             t.slab_rows = req->slab_rows;
     }
-    if (K * row_bytes >= kHubMinBBytes) {
+    if ((uint64_t)K * (uint64_t)row_bytes >= (uint64_t)kHubMinBBytes) {  // < 2^64: no wrap
         const int64_t n_slabs = (K + t.slab_rows - 1) / t.slab_rows;
         int64_t h = kHubEntriesPerSlab * n_slabs;
         h = h < t.medium_max ? t.medium_max : (h > INT32_MAX ? INT32_MAX : h);

@@ -308,7 +308,7 @@ def test_bf16_empty_and_widened_shapes():
     exact fp32 copy of C, B and D: within the bound of the oracle, and, in
     the rows that are not split across wavefronts (split rows meet in fp32
     atomic adds, in no fixed order), bit for bit what fusedmm_csr_f32 gives
-    on the widened values."""
+    on the widened values; a row view of the same rows gives the same."""
     rng = np.random.default_rng(17)
     M, K = 40, 30
     E = run_fused_bf16(np.zeros(M + 1, np.int32), np.zeros(0, np.int32),
@@ -327,5 +327,10 @@ def test_bf16_empty_and_widened_shapes():
         whole = np.diff(rp) <= sdl.resolve_tuning(sdl.DTYPE_F32, N, K=K).medium_max
         assert whole.sum() > M // 2
         assert np.array_equal(E[whole], E32[whole]), (N, shift)
+        if N == 12:
+            # a row view (rowptr[0] = 5): the same rows, bit for bit
+            Ev = run_fused_bf16(rp + 5, np.concatenate([np.zeros(5, np.int32), ci]),
+                                C, B, D, M, K, N)
+            assert np.array_equal(Ev[whole], E[whole])
 
 
