@@ -112,7 +112,7 @@ void noalloc_arguments()
 void resolve_tuning()
 {
     const int64_t Ks[] = {0, 1, 1024, 262144, 1048576, (int64_t{1} << 31) - 1};
-    const int64_t Ns[] = {1, 3, 32, 64, 256, 512, 1000, 4096};
+    const int64_t Ns[] = {1, 3, 32, 64, 256, 512, 1000, 4096, (int64_t{1} << 31) - 1};
     for (int dtype = 0; dtype < 2; ++dtype)
         for (int64_t K : Ks)
             for (int64_t N : Ns) {
