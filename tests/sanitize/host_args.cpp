@@ -183,6 +183,9 @@ void sddmm_fusedmm_arguments()
                                      nullptr) == SPMM_ERROR_INVALID_VALUE);
     EXPECT(fusedmm_csr_bf16in_f32acc(rp, rp, fake<const uint16_t>(1), h, h, o, 4, 4, 8, 3,
                                      nullptr) == SPMM_ERROR_INVALID_VALUE);
+    const int64_t big = (int64_t{1} << 31) - 1;  // widened copy past 2^56 bytes
+    EXPECT(fusedmm_csr_bf16in_f32acc(rp, rp, h, h, h, o, big, big, big, 3, nullptr) ==
+           SPMM_ERROR_OUT_OF_MEMORY);
 }
 
 void hooks_and_timing()
