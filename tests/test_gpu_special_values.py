@@ -103,11 +103,12 @@ def check_values(got, ref, S, tol, what):
     assert np.all(err <= tol * S[fin] + ABS), f"{what}: finite values"
 
 
-@pytest.mark.parametrize("dtype,N", [("bf16", 256), ("f32", 64)])
+@pytest.mark.parametrize("dtype,N", [("bf16", 256), ("bf16", 12), ("f32", 64)])
 def test_special_values_sddmm_fusedmm(dtype, N):
     """SDDMM values and FusedMM rows with infinities and NaN in B: each dot
     product (bf16: by dot-product instructions over column pairs) is
-    non-finite exactly where IEEE arithmetic makes it so."""
+    non-finite exactly where IEEE arithmetic makes it so.  bf16 at N = 12
+    takes FusedMM's widened fp32 copy."""
     p = problem(dtype, N, seed=131 + N, M=1500)
     rng = np.random.default_rng(131)
     x = rng.uniform(-1, 1, (p.M, p.N)).astype(np.float32)
